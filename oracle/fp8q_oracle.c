@@ -1,0 +1,346 @@
+/*
+ * fp8q oracle -- a plain, slow, deliberately obvious CPU implementation of
+ * amax-scaled FP8 quantization and the block-scaled FP8 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the yardstick the GPU library is
+ * checked against; it is never part of the product path.  Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg load it.  It
+ * shares no header, table, helper or constant generator with the HIP code.
+ *
+ * Arithmetic: fp64 or exact integers wherever the method leaves a choice;
+ * fp32 exactly where the method itself computes in fp32 (x/s, amax/MAX,
+ * q*s).  Build with  gcc -O2 -fno-fast-math -ffp-contract=off  so every
+ * float operation is one IEEE-754 binary32 operation (x86-64 SSE).
+ *
+ * Sources.  [A] = the PyTorch-native FP8 article at m.nxbn.cn/news/137885;
+ * its sections are cited by its own numbers (1.2 format table, 1.3 "FN"
+ * semantics, 2.2 scalar experiment, 4.1-4.3 scale factors / DelayedScaler).
+ * [H] = the handbook chapter "混合精度与 FP8 训练" (anrans.github.io
+ * ai-infra-handbooks), section "FP8 训练" (quant, per_tensor, per_block,
+ * rel_err and the hardware notes on 128-element promotion) and its second
+ * exercise (one outlier of 5000).
+ *
+ * Readings where the pages are silent or disagree (each also listed in the
+ * design notes): 0x7F/0xFF of E4M3FN are NaN (max finite is 448 per [A] 1.2
+ * and [H]); E5M2 exponent 31 is Inf (m=0) / NaN; rounding is
+ * round-to-nearest-even; overflow saturates to +-MAX for both formats;
+ * signed zero is kept; a NaN input encodes as 0x7F; NaN propagates through
+ * amax; scales are dequant scales s = max(amax, eps)*margin / MAX.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_E4M3FN 0
+#define ORC_E5M2 1
+#define ORC_F32 0
+#define ORC_BF16 1
+#define ORC_GRAN_TENSOR 0
+#define ORC_GRAN_1x128 1
+#define ORC_GRAN_128x128 2
+
+/* ------------------------------------------------------------------ */
+/* Format parameters, [A] 1.2: E4M3 = 1/4/3 bits, bias 7, max 448;     */
+/* E5M2 = 1/5/2 bits, bias 15, max 57344.                              */
+/* ------------------------------------------------------------------ */
+static int mant_bits(int fmt) { return fmt == ORC_E4M3FN ? 3 : 2; }
+static int exp_bias(int fmt) { return fmt == ORC_E4M3FN ? 7 : 15; }
+
+double orc_max_finite(int fmt) { return fmt == ORC_E4M3FN ? 448.0 : 57344.0; }
+
+/* bf16 is the top half of a binary32; widening is exact. */
+static float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+static float load_elem(const void* x, int dt, int64_t i) {
+  if (dt == ORC_F32) return ((const float*)x)[i];
+  return bf16_to_f32(((const uint16_t*)x)[i]);
+}
+
+static float canonical_nan(void) {
+  uint32_t u = 0x7FC00000u;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* ------------------------------------------------------------------ */
+/* decode one code to its exact value (every FP8 value is exact in */
+/* double).  Field widths and bias from [A] 1.2.                       */
+/* ------------------------------------------------------------------ */
+double orc_decode(uint32_t code, int fmt) {
+  code &= 0xFF;
+  double sign = (code & 0x80) ? -1.0 : 1.0;
+  int M = mant_bits(fmt), bias = exp_bias(fmt);
+  int e = (int)((code & 0x7F) >> M);
+  int m = (int)(code & ((1u << M) - 1));
+  if (fmt == ORC_E4M3FN) {
+    if (e == 15 && m == 7) return NAN; /* only NaN pattern, no Inf */
+  } else {
+    if (e == 31) return m == 0 ? sign * INFINITY : NAN;
+  }
+  if (e == 0) /* subnormal: m * 2^(1 - bias - M) */
+    return sign * ldexp((double)m, 1 - bias - M);
+  return sign * ldexp((double)((1 << M) + m), e - bias - M);
+}
+
+/* ------------------------------------------------------------------ */
+/* saturating round-to-nearest-even encoder (encoder "A").         */
+/* Every rescaling below is by a power of two, so it is exact in       */
+/* double; nearbyint() rounds half to even in the default mode.        */
+/* ------------------------------------------------------------------ */
+uint32_t orc_encode(float v, int fmt) {
+  if (isnan(v)) return 0x7F;
+  int M = mant_bits(fmt), bias = exp_bias(fmt);
+  int emin = 1 - bias; /* exponent of the smallest normal */
+  uint32_t sgn = signbit(v) ? 0x80u : 0u;
+  double a = fabs((double)v);
+  double maxv = orc_max_finite(fmt);
+  if (a > maxv) a = maxv; /* saturate; +-Inf also lands here */
+  if (a < ldexp(1.0, emin)) {
+    /* subnormal range: a count of quanta 2^(emin-M); k == 2^M is exactly
+       the code of the smallest normal, so no special case is needed */
+    double k = nearbyint(ldexp(a, M - emin));
+    return sgn | (uint32_t)k;
+  }
+  int E;
+  (void)frexp(a, &E);
+  E -= 1; /* a = f * 2^E with f in [1, 2) */
+  double k = nearbyint(ldexp(a, M - E)); /* in [2^M, 2^(M+1)] */
+  if (k == ldexp(1.0, M + 1)) {          /* rounded up into the next binade */
+    E += 1;
+    k = ldexp(1.0, M);
+  }
+  return sgn | ((uint32_t)(E + bias) << M) | (uint32_t)(k - ldexp(1.0, M));
+}
+
+/* Encode a whole fp32 buffer (used by the exhaustive cross-checks). */
+void orc_encode_array(const float* v, int64_t n, int fmt, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_encode(v[i], fmt);
+}
+
+/* Encode the fp32 values whose bit patterns are lo, lo+1, ..., lo+n-1. */
+void orc_encode_bits_range(uint32_t lo, int64_t n, int fmt, uint8_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t u = lo + (uint32_t)i;
+    float f;
+    memcpy(&f, &u, 4);
+    out[i] = (uint8_t)orc_encode(f, fmt);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* amax = max |x| over a granule; a NaN anywhere makes it NaN.     */
+/* ([A] 4.1 and 4.2 update(); [H] per_tensor / per_block)              */
+/* ------------------------------------------------------------------ */
+float orc_amax(const void* x, int dt, int64_t n) {
+  float m = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(load_elem(x, dt, i));
+    if (isnan(a)) return canonical_nan();
+    if (a > m) m = a;
+  }
+  return m;
+}
+
+/* ------------------------------------------------------------------ */
+/* dequant scale s = fl32(fl32(max(amax, eps) * margin) / MAX).    */
+/* [H] per_block: amax.clamp(min=1e-12) / MAX; [A] 4.3 margin.         */
+/* A NaN amax gives a NaN scale (the comparison below is false).       */
+/* ------------------------------------------------------------------ */
+float orc_scale(float amax, float max_val, float eps, float margin) {
+  float m = (amax < eps) ? eps : amax;
+  float t = m * margin;
+  return t / max_val;
+}
+
+/* one element, q = enc(fl32(x / s)); [H] quant: (x / s).clamp().to(FP8) */
+uint32_t orc_quantize_value(float x, float s, int fmt) {
+  float y = x / s;
+  return orc_encode(y, fmt);
+}
+
+/* ------------------------------------------------------------------ */
+/* granule drivers                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Per-tensor (or delayed) scaling with a given dequant scale s. */
+void orc_quantize_tensor(const void* x, int dt, int64_t n, int fmt, float s, uint8_t* q) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) q[i] = (uint8_t)orc_quantize_value(load_elem(x, dt, i), s, fmt);
+}
+
+/* Block scaling with br x bc blocks ([H] per_block: reshape into
+   (R/br, br, C/bc, bc), amax over dims (1,3), clamp, / MAX).
+   Element (r, c) lives at x[r*ldx + c]; its code at q[r*ldq + c];
+   the scale of block (rb, cb) at scales[rb*ld_s + cb]. */
+void orc_quantize_blocks(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx,
+                         int64_t br, int64_t bc, int fmt, float eps, uint8_t* q, int64_t ldq,
+                         float* scales, int64_t ld_s) {
+  int64_t nrb = rows / br, ncb = cols / bc;
+  float max_val = (float)orc_max_finite(fmt);
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t rb = 0; rb < nrb; ++rb) {
+    for (int64_t cb = 0; cb < ncb; ++cb) {
+      float amax = 0.0f;
+      int has_nan = 0;
+      for (int64_t r = rb * br; r < (rb + 1) * br; ++r)
+        for (int64_t c = cb * bc; c < (cb + 1) * bc; ++c) {
+          float a = fabsf(load_elem(x, dt, r * ldx + c));
+          if (isnan(a)) has_nan = 1;
+          else if (a > amax) amax = a;
+        }
+      if (has_nan) amax = canonical_nan();
+      float s = orc_scale(amax, max_val, eps, 1.0f);
+      scales[rb * ld_s + cb] = s;
+      for (int64_t r = rb * br; r < (rb + 1) * br; ++r)
+        for (int64_t c = cb * bc; c < (cb + 1) * bc; ++c)
+          q[r * ldq + c] = (uint8_t)orc_quantize_value(load_elem(x, dt, r * ldx + c), s, fmt);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* dequantize x^ = fl32(dec(q) * s), optionally rounded to bf16.   */
+/* [H] quant: .float() * scale.  dec(q) has <= 4 significant bits and s */
+/* 24, so the double product is exact and the cast rounds once.        */
+/* ------------------------------------------------------------------ */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if (isnan(f)) return 0x7FC0;
+  uint32_t lsb = (u >> 16) & 1u;
+  u += 0x7FFFu + lsb;
+  return (uint16_t)(u >> 16);
+}
+
+void orc_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
+                    const float* scales, int gran, int64_t ld_s, void* y, int out_dt, int64_t ldy) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      float s;
+      if (gran == ORC_GRAN_TENSOR) s = scales[0];
+      else if (gran == ORC_GRAN_1x128) s = scales[r * ld_s + c / 128];
+      else s = scales[(r / 128) * ld_s + c / 128];
+      float v = (float)(orc_decode(q[r * ldq + c], fmt) * (double)s);
+      if (out_dt == ORC_F32) ((float*)y)[r * ldy + c] = v;
+      else ((uint16_t*)y)[r * ldy + c] = f32_to_bf16_rne(v);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* delayed scaling ([A] 4.2 DelayedScaler): a window of the last    */
+/* `window` amax values; once it is full, the scale becomes             */
+/* scale(max(window)); until then it stays at its initial 1.0.  The     */
+/* scale in force at step t quantizes x_t; amax(x_t) is pushed after.   */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  float ring[1024];
+  int32_t window, count, pos;
+  float max_val, eps, margin;
+  float scale;
+} orc_scaler;
+
+int orc_scaler_init(orc_scaler* st, int32_t window, float max_val, float eps, float margin) {
+  if (window < 1 || window > 1024) return 1;
+  memset(st, 0, sizeof(*st));
+  st->window = window;
+  st->max_val = max_val;
+  st->eps = eps;
+  st->margin = margin;
+  st->scale = 1.0f;
+  return 0;
+}
+
+void orc_scaler_update(orc_scaler* st, float amax) {
+  st->ring[st->pos] = amax;
+  st->pos = (st->pos + 1) % st->window;
+  if (st->count < st->window) st->count += 1;
+  if (st->count >= st->window) {
+    float m = 0.0f;
+    int has_nan = 0;
+    for (int32_t i = 0; i < st->window; ++i) {
+      if (isnan(st->ring[i])) has_nan = 1;
+      else if (st->ring[i] > m) m = st->ring[i];
+    }
+    if (has_nan) m = canonical_nan();
+    st->scale = orc_scale(m, st->max_val, st->eps, st->margin);
+  }
+}
+
+int64_t orc_scaler_size(void) { return (int64_t)sizeof(orc_scaler); }
+
+/* ------------------------------------------------------------------ */
+/* block-scaled GEMM                                               */
+/*   C[m,n] = sum_kb (sA[m,kb] * sB[.,kb]) * P_kb[m,n],                 */
+/*   P_kb[m,n] = sum_{k in block kb} dec(A[m,k]) * dec(B[n,k]).         */
+/* ([H] per-op table: FP8 inputs with fp32 accumulation; hardware      */
+/* notes: partial sums promoted every 128 elements of K.)               */
+/* Every finite E4M3 value is an integer multiple of 2^-9 and every     */
+/* E5M2 value a multiple of 2^-16, so dec(.) * 2^16 is an integer and   */
+/* P_kb * 2^32 is an exact __int128 sum.  The coefficient sA*sB is      */
+/* exact in double (24 x 24 bits).  The outer sum over kb is fp64.      */
+/* D[m,n] = sum_kb |sA*sB| * sum_k |dec(a)*dec(b)| is the scale of the  */
+/* rounding error any fp32 evaluation may commit.                       */
+/* A NaN or Inf code anywhere in a dot product makes C NaN there.       */
+/* ------------------------------------------------------------------ */
+static void int_table(int fmt, int64_t tab[256], unsigned char ok[256]) {
+  for (uint32_t c = 0; c < 256; ++c) {
+    double v = orc_decode(c, fmt);
+    ok[c] = (unsigned char)(isfinite(v) != 0);
+    tab[c] = ok[c] ? (int64_t)ldexp(v, 16) : 0; /* exact: v is a multiple of 2^-16 */
+  }
+}
+
+void orc_gemm_blockscaled(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm,
+                          int64_t sA_skb, const uint8_t* B, int fb, int64_t ldb, const float* sB,
+                          int gb, int64_t sB_sn, int64_t sB_skb, int64_t M, int64_t N, int64_t K,
+                          const int64_t* rows, int64_t nrows, double* C, double* D) {
+  int64_t ta[256], tb[256];
+  unsigned char oka[256], okb[256];
+  int_table(fa, ta, oka);
+  int_table(fb, tb, okb);
+  int64_t nkb = K / 128;
+  int64_t nr = rows ? nrows : M;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ri = 0; ri < nr; ++ri) {
+    int64_t m = rows ? rows[ri] : ri;
+    const uint8_t* arow = A + m * lda;
+    for (int64_t n = 0; n < N; ++n) {
+      const uint8_t* brow = B + n * ldb;
+      double c = 0.0, d = 0.0;
+      int special = 0;
+      for (int64_t kb = 0; kb < nkb; ++kb) {
+        __int128 p = 0, pabs = 0;
+        for (int64_t k = kb * 128; k < kb * 128 + 128; ++k) {
+          if (!oka[arow[k]] || !okb[brow[k]]) {
+            special = 1;
+            continue;
+          }
+          __int128 t = (__int128)ta[arow[k]] * (__int128)tb[brow[k]];
+          p += t;
+          pabs += t < 0 ? -t : t;
+        }
+        double sa = (double)sA[m * sA_sm + kb * sA_skb];
+        double sb = (gb == ORC_GRAN_128x128) ? (double)sB[(n / 128) * sB_sn + kb * sB_skb]
+                                              : (double)sB[n * sB_sn + kb * sB_skb];
+        double coef = sa * sb; /* exact */
+        c += coef * ldexp((double)p, -32);
+        d += fabs(coef) * ldexp((double)pabs, -32);
+      }
+      if (special) c = NAN;
+      C[ri * N + n] = c;
+      D[ri * N + n] = d;
+    }
+  }
+}
+
+int orc_version(void) { return 1; }

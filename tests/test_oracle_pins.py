@@ -1,0 +1,454 @@
+"""Pins for the CPU oracle: facts the pages and the mathematics fix, checked
+without trusting the oracle's own formulas.
+
+Each test names what pins it: a printed value on a page (tests/golden/*),
+a closed form, an invariant, an independent brute force, or a library
+routine (torch's float8/bf16 casts, numpy's IEEE float32 arithmetic,
+Python's exact Fractions).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from conftest import golden
+
+E4, E5 = 0, 1
+FMT_NAME = {E4: "E4M3FN", E5: "E5M2"}
+MAXF = {E4: 448.0, E5: 57344.0}
+MAXCODE = {E4: 0x7E, E5: 0x7B}
+TORCH_FP8 = {E4: torch.float8_e4m3fn, E5: torch.float8_e5m2}
+
+
+def f32(v):
+    return np.float32(v)
+
+
+def bits_to_f32(u):
+    return np.array([u], dtype=np.uint32).view(np.float32)[0]
+
+
+# ------------------------------------------------------------------ format table / decode
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_format_table_extremes(orc, fmt):
+    """PyTorch-native FP8 article, section 1.2 table: max finite, min normal, min subnormal, bias."""
+    g = golden("format_table.json")[FMT_NAME[fmt]]
+    M, bias = g["mant_bits"], g["bias"]
+    assert orc.decode(MAXCODE[fmt], fmt) == g["max_finite"]
+    assert orc.decode(1 << M, fmt) == 2.0 ** (1 - bias)       # smallest normal: e=1, m=0
+    assert orc.decode(1, fmt) == 2.0 ** (1 - bias - M)        # smallest subnormal: e=0, m=1
+    assert orc.decode(bias << M, fmt) == 1.0                  # the exponent bias puts 1.0 at e=bias
+    if fmt == E4:
+        assert orc.decode(1 << M, fmt) == g["min_normal"]
+        assert orc.decode(1, fmt) == g["min_subnormal"]
+    else:
+        assert orc.decode(1 << M, fmt) == 2.0 ** g["min_normal_pow2"]
+        assert abs(orc.decode(1 << M, fmt) - g["min_normal_approx"]) < 1e-6
+        assert orc.decode(1, fmt) == 2.0 ** g["min_subnormal_pow2"]
+        assert abs(orc.decode(1, fmt) - g["min_subnormal_approx"]) < 1e-7
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_decode_exhaustive_structure(orc, fmt):
+    """All 256 codes: special-value counts, strict monotonicity of the positive
+    finite codes, and sign symmetry (the readings: E4M3FN has only 0x7F/0xFF as
+    NaN, E5M2 has IEEE-style Inf/NaN at exponent 31)."""
+    t = orc.decode_table(fmt)
+    nan = np.isnan(t)
+    inf = np.isinf(t)
+    if fmt == E4:
+        assert nan.sum() == 2 and inf.sum() == 0
+        assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    else:
+        assert nan.sum() == 6 and inf.sum() == 2
+        assert list(np.nonzero(inf)[0]) == [0x7C, 0xFC]
+    fin = ~(nan | inf)
+    assert fin.sum() == (254 if fmt == E4 else 248)
+    pos = [t[c] for c in range(128) if fin[c]]
+    assert all(b > a for a, b in zip(pos, pos[1:]))
+    assert pos[0] == 0.0 and pos[-1] == MAXF[fmt]
+    for c in range(128):
+        if fin[c]:
+            assert t[c | 0x80] == -t[c]
+    assert math.copysign(1.0, t[0x80]) == -1.0  # signed zero
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_decode_matches_torch(orc, fmt):
+    """Library routine: torch's float8 dtypes decode all 256 bit patterns."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(TORCH_FP8[fmt]).to(torch.float64).numpy()
+    t = orc.decode_table(fmt)
+    assert np.array_equal(np.isnan(ref), np.isnan(t))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], t[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(t[ok]))
+
+
+# ------------------------------------------------------------------ encoder
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_scalar_experiment(orc, fmt):
+    """PyTorch-native FP8 article, section 2.2: the scalar experiment."""
+    g = golden("scalar_experiment.json")
+    for v, code, val in zip(g["inputs"], g[FMT_NAME[fmt]]["codes"], g[FMT_NAME[fmt]]["values"]):
+        c = orc.encode(v, fmt)
+        assert c == code, (v, hex(c), hex(code))
+        assert orc.decode(c, fmt) == val
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_round_trip_and_saturation(orc, fmt):
+    """Invariant: enc(dec(c)) == c for every finite code (incl. -0 = 0x80);
+    every |v| >= MAX and +-Inf saturate; NaN gives 0x7F."""
+    for c in range(256):
+        v = orc.decode(c, fmt)
+        if math.isnan(v):
+            continue
+        if math.isinf(v):
+            assert orc.encode(v, fmt) == (MAXCODE[fmt] | (c & 0x80))
+            continue
+        assert orc.encode(v, fmt) == c, hex(c)
+    for v in (MAXF[fmt], MAXF[fmt] * 1.0001, 1e30, 3.4e38, float("inf")):
+        assert orc.encode(v, fmt) == MAXCODE[fmt]
+        assert orc.encode(-v, fmt) == MAXCODE[fmt] | 0x80
+    assert orc.encode(float("nan"), fmt) == 0x7F
+    assert orc.encode(-float("nan"), fmt) == 0x7F
+    assert orc.encode(-0.0, fmt) == 0x80
+    assert orc.encode(-1e-30, fmt) == 0x80
+
+
+def _band(fmt):
+    """fp32 binades that can produce a nonzero, non-saturated code, one extra on each side."""
+    lo_exp, hi_exp = (-12, 9) if fmt == E4 else (-19, 16)
+    return (127 + lo_exp) << 23, (127 + hi_exp + 1) << 23
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encoder_matches_bruteforce_band(orc, encb, fmt):
+    """Independent brute force (nearest listed value, ties to even code) on
+    every non-negative fp32 pattern in the band where codes are non-trivial,
+    plus a strided sample of all 2^32 patterns (both signs, subnormals, Inf,
+    NaN)."""
+    lo, hi = _band(fmt)
+    chunk = 1 << 25
+    for start in range(lo, hi, chunk):
+        n = min(chunk, hi - start)
+        a = orc.encode_bits_range(start, n, fmt)
+        b = np.empty(n, dtype=np.uint8)
+        encb.encb_bits(start, 1, n, fmt, b.ctypes.data)
+        bad = np.nonzero(a != b)[0]
+        assert bad.size == 0, (hex(start + int(bad[0])), hex(a[bad[0]]), hex(b[bad[0]]))
+    stride = 4093
+    n = (1 << 32) // stride
+    b = np.empty(n, dtype=np.uint8)
+    encb.encb_bits(0, stride, n, fmt, b.ctypes.data)
+    u = (np.arange(n, dtype=np.uint64) * stride).astype(np.uint32)
+    a = orc.encode_array(u.view(np.float32), fmt)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.skipif(os.environ.get("FP8Q_EXHAUSTIVE") != "1", reason="set FP8Q_EXHAUSTIVE=1 for all 2^32 patterns")
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encoder_matches_bruteforce_all_2p32(orc, encb, fmt):
+    chunk = 1 << 26
+    for start in range(0, 1 << 32, chunk):
+        a = orc.encode_bits_range(start, chunk, fmt)
+        b = np.empty(chunk, dtype=np.uint8)
+        encb.encb_bits(start, 1, chunk, fmt, b.ctypes.data)
+        assert np.array_equal(a, b), hex(start)
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encoder_matches_torch_cast(orc, fmt):
+    """Library routine: torch's RNE float8 cast after clamping to +-MAX (the
+    handbook's quant clamps before the cast).  Every bf16 pattern, and a
+    random sample of fp32 patterns; NaN excluded (torch keeps its sign)."""
+    h = np.arange(1 << 16, dtype=np.uint32) << 16
+    r = np.random.default_rng(0).integers(0, 1 << 32, size=1 << 22, dtype=np.uint64).astype(np.uint32)
+    for u in (h, r):
+        x = u.view(np.float32)
+        x = x[~np.isnan(x)]
+        ref = torch.from_numpy(x.copy()).clamp(-MAXF[fmt], MAXF[fmt]).to(TORCH_FP8[fmt]).view(torch.uint8).numpy()
+        assert np.array_equal(orc.encode_array(x, fmt), ref)
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_encoder_sign_symmetry(orc, fmt):
+    """Invariant: code(-v) = code(v) | 0x80 for every non-NaN v."""
+    r = np.random.default_rng(1).integers(0, 1 << 31, size=1 << 20, dtype=np.uint64).astype(np.uint32)
+    x = r.view(np.float32)
+    x = x[~np.isnan(x)]
+    assert np.array_equal(orc.encode_array(-x, fmt), orc.encode_array(x, fmt) | 0x80)
+
+
+# ------------------------------------------------------------------ amax / scale / quantize
+def test_amax_cases(orc):
+    x = np.array([0.5, -3.0, 2.0, -0.0], dtype=np.float32)
+    assert orc.amax(x) == 3.0
+    assert orc.amax(np.zeros(7, np.float32)) == 0.0
+    assert orc.amax(np.array([1.0, -np.inf], np.float32)) == np.inf
+    m = orc.amax(np.array([1.0, np.nan, 5.0], np.float32))
+    assert np.isnan(m) and np.array([m], np.float32).view(np.uint32)[0] == 0x7FC00000
+    # bf16 is widened exactly: 0xC040 = -3.0, 0x3F80 = 1.0
+    assert orc.amax(np.array([0x3F80, 0xC040], np.uint16)) == 3.0
+    rng = np.random.default_rng(2)
+    y = rng.standard_normal(100_003).astype(np.float32)
+    assert orc.amax(y) == np.abs(y).max()  # library reduction
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_scale_closed_forms(orc, fmt):
+    """s = fl32(max(amax, eps) * margin / MAX): exact powers of two for
+    amax = MAX * 2^k; the eps clamp for an all-zero granule; IEEE float32
+    division (numpy) elsewhere."""
+    for k in range(-20, 21):
+        assert orc.scale(MAXF[fmt] * 2.0 ** k, fmt) == f32(2.0 ** k)
+    eps = f32(1e-12)
+    assert orc.scale(0.0, fmt) == eps / f32(MAXF[fmt])
+    assert np.isnan(orc.scale(float("nan"), fmt))
+    rng = np.random.default_rng(3)
+    a = (rng.random(1000) * 1e4).astype(np.float32)
+    for v in a[:200]:
+        assert orc.scale(v, fmt) == f32(v) / f32(MAXF[fmt])
+        assert orc.scale(v, fmt, margin=1.1) == (f32(v) * f32(1.1)) / f32(MAXF[fmt])
+
+
+def test_exercise_outlier_5000(orc):
+    """Handbook exercise 2: one value of 5000 sets the per-tensor scale to
+    5000/448 ~ 11.2 and 0.01 quantizes to 0."""
+    g = golden("exercise_outlier5000.json")
+    x = np.concatenate([np.linspace(-1, 1, 1001, dtype=np.float32), np.array([g["outlier"]], np.float32)])
+    s = orc.scale(orc.amax(x), E4)
+    assert round(float(s), g["scale_approx_digits"]) == g["scale_approx"]
+    assert float(s) == float(f32(5000.0) / f32(448.0))
+    assert orc.quantize_value(g["small_value"], s, E4) == g["small_value_code"]
+    qv = g["small_value"] / float(s)
+    assert abs(qv - g["quotient_approx"]) < 0.00005 and qv < g["min_subnormal"] / 2
+    q = orc.quantize_tensor(x, E4, s)
+    deq = orc.decode_table(E4)[q] * float(s)
+    inner = np.abs(x) <= 1
+    # "only one or two significant digits": relative error of nonzero results
+    # in [-1, 1] is large compared with E4M3's own 2^-4
+    nz = inner & (deq != 0)
+    assert np.max(np.abs(deq[nz] - x[nz]) / np.abs(x[nz])) > 0.1
+    assert orc.quantize_value(5000.0, s, E4) == 0x7E
+
+
+def _outlier_errors(orc, a):
+    x = a.numpy()
+    s = orc.scale(orc.amax(x), E4)
+    q = orc.quantize_tensor(x, E4, s)
+    y = orc.dequantize(q.reshape(x.shape), E4, np.array([s], np.float32), orc.GRAN_TENSOR)
+    qb, sb = orc.quantize_1x128(x, E4)
+    yb = orc.dequantize(qb, E4, sb, orc.GRAN_1x128)
+    return orc.rel_err(y[:, 128:], x[:, 128:]), orc.rel_err(yb[:, 128:], x[:, 128:])
+
+
+def test_outlier_experiment_printed_table(orc):
+    """Handbook 'FP8 训练': the printed per-tensor vs per-1x128 table, reproduced
+    digit for digit from the same seeded torch.randn inputs."""
+    g = golden("outlier_experiment.json")
+    torch.manual_seed(g["seed"])
+    for f, pt, pb in zip(g["factors"], g["per_tensor_pct"], g["per_1x128_pct"]):
+        a = torch.randn(*g["shape"])
+        a[:, : g["outlier_cols"]] *= f
+        t, b = _outlier_errors(orc, a)
+        assert round(100 * t, 1) == pt, (f, t)
+        assert round(100 * b, 1) == pb, (f, b)
+
+
+def test_outlier_experiment_other_seeds(orc):
+    """The same experiment's claim for any seed: 1x128 error stays near 2.6%
+    (E4M3's own precision); per-tensor error grows with the outlier."""
+    for seed in (1, 2, 3):
+        torch.manual_seed(seed)
+        prev = 0.0
+        for f in (1e2, 1e4, 3e4):
+            a = torch.randn(256, 1024)
+            a[:, :4] *= f
+            t, b = _outlier_errors(orc, a)
+            assert 0.024 <= b <= 0.028
+            assert t > prev
+            prev = t
+        assert prev > 0.10
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("br,bc", [(1, 128), (128, 128)])
+def test_block_quantize_invariants(orc, fmt, br, bc):
+    """Each block's scale is scale(amax of the block) (numpy reduction and
+    float32 division); the block's largest-magnitude element encodes to
+    +-MAX; every code equals the per-element quantize with its block's
+    scale; an all-zero block takes the eps scale and codes 0x00 / 0x80."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((256, 384)) * np.exp(rng.standard_normal((256, 1)) * 3)).astype(np.float32)
+    x[0:128, 0:128] = 0.0
+    x[5, 7] = -0.0
+    q, s = orc.quantize_blocks(x, br, bc, fmt)
+    for rb in range(256 // br):
+        for cb in range(384 // bc):
+            blk = x[rb * br:(rb + 1) * br, cb * bc:(cb + 1) * bc]
+            am = np.abs(blk).max()
+            want = max(am, f32(1e-12)) / f32(MAXF[fmt])
+            assert s[rb, cb] == f32(want)
+            qb = q[rb * br:(rb + 1) * br, cb * bc:(cb + 1) * bc]
+            if am > 0:
+                i = np.unravel_index(np.argmax(np.abs(blk)), blk.shape)
+                assert qb[i] & 0x7F == MAXCODE[fmt]
+            else:
+                assert set(np.unique(qb)) <= {0x00, 0x80}
+    assert q[5, 7] == 0x80
+    for (r, c) in [(3, 200), (200, 3), (255, 383), (130, 129)]:
+        assert q[r, c] == orc.quantize_value(x[r, c], s[r // br, c // bc], fmt)
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_dequantize_is_one_float32_product(orc, fmt):
+    """x^ = fl32(dec(q) * s): numpy's IEEE float32 multiply of the decoded
+    value; the bf16 output is torch's round-to-nearest-even bf16 cast."""
+    rng = np.random.default_rng(5)
+    q = np.tile(np.arange(256, dtype=np.uint8), 8).reshape(8, 256)
+    t = orc.decode_table(fmt)
+    fin = ~np.isnan(t) & ~np.isinf(t)
+    q = np.where(fin[q], q, 0).astype(np.uint8)
+    s = (rng.random((8, 2)) * 10 + 1e-3).astype(np.float32)
+    y = orc.dequantize(q, fmt, s, orc.GRAN_1x128)
+    ref = t[q].astype(np.float32) * np.repeat(s, 128, axis=1)
+    assert np.array_equal(y, ref)
+    yb = orc.dequantize(q, fmt, s, orc.GRAN_1x128, out_bf16=True)
+    refb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(yb, refb)
+
+
+# ------------------------------------------------------------------ delayed scaler
+def test_delayed_scaler_ramp_closed_form(orc):
+    """PyTorch-native FP8 article, section 4.2 DelayedScaler(window=16): the
+    scale starts at 1.0, stays there until 16 amaxes are seen, then is
+    max(last 16 amax) / 448.  With amax_t = t + 1 the scale in force at step
+    t >= 16 is fl32(t / 448)."""
+    st = orc.scaler_new(16, E4)
+    for t in range(64):
+        used = st.scale
+        if t <= 15:
+            assert used == 1.0
+        else:
+            assert used == f32(t) / f32(448.0)
+        orc.scaler_update(st, float(t + 1))
+    assert st.count == 16 and st.pos == 64 % 16
+
+
+def test_delayed_scaler_spike_is_forgotten(orc):
+    """A spike at step j sets the scale for steps j+1 .. j+16 and is gone at j+17."""
+    j = 30
+    st = orc.scaler_new(16, E5)
+    used = []
+    for t in range(80):
+        used.append(st.scale)
+        orc.scaler_update(st, 1000.0 if t == j else 2.0)
+    spike = f32(1000.0) / f32(57344.0)
+    base = f32(2.0) / f32(57344.0)
+    for t in range(80):
+        if t < 16:
+            assert used[t] == 1.0
+        elif j + 1 <= t <= j + 16:
+            assert used[t] == spike, t
+        else:
+            assert used[t] == base, t
+
+
+def test_window_one_is_current_scaling(orc):
+    st = orc.scaler_new(1, E4)
+    rng = np.random.default_rng(6)
+    for a in rng.random(20) * 100:
+        orc.scaler_update(st, a)
+        assert st.scale == orc.scale(a, E4)
+    with pytest.raises(ValueError):
+        orc.scaler_new(0, E4)
+
+
+# ------------------------------------------------------------------ GEMM
+def _rand_codes(rng, shape, fmt, lim=None):
+    t_ok = {E4: [c for c in range(256) if c not in (0x7F, 0xFF)],
+            E5: [c for c in range(256) if (c & 0x7F) < 0x7C]}[fmt]
+    return rng.choice(np.array(t_ok, dtype=np.uint8), size=shape)
+
+
+def _exact_gemm(orc, A, fa, sA, B, fb, sB, gb):
+    ta = {c: Fraction(orc.decode(c, fa)) for c in range(256) if math.isfinite(orc.decode(c, fa))}
+    tb = {c: Fraction(orc.decode(c, fb)) for c in range(256) if math.isfinite(orc.decode(c, fb))}
+    M, K = A.shape
+    N = B.shape[0]
+    C = np.empty((M, N))
+    D = np.empty((M, N))
+    for m in range(M):
+        for n in range(N):
+            c = Fraction(0)
+            d = Fraction(0)
+            for kb in range(K // 128):
+                coef = Fraction(float(sA[m, kb])) * Fraction(float(sB[n // 128, kb] if gb == 2 else sB[n, kb]))
+                p = sum((ta[A[m, k]] * tb[B[n, k]] for k in range(kb * 128, kb * 128 + 128)), Fraction(0))
+                pa = sum((abs(ta[A[m, k]] * tb[B[n, k]]) for k in range(kb * 128, kb * 128 + 128)), Fraction(0))
+                c += coef * p
+                d += abs(coef) * pa
+            C[m, n] = float(c)
+            D[m, n] = float(d)
+    return C, D
+
+
+@pytest.mark.parametrize("fa,fb,gb", [(E4, E4, 2), (E5, E4, 2), (E5, E4, 1), (E5, E5, 1), (E4, E5, 2)])
+def test_gemm_matches_exact_rationals(orc, fa, fb, gb):
+    """Brute force in exact rational arithmetic (Fractions) on tiny inputs."""
+    rng = np.random.default_rng(7)
+    M, N, K = 2, 256, 256
+    A = _rand_codes(rng, (M, K), fa)
+    B = _rand_codes(rng, (N, K), fb)
+    sA = (rng.random((M, K // 128)) * 3 + 0.01).astype(np.float32)
+    sB = (rng.random(((N // 128) if gb == 2 else N, K // 128)) * 3 + 0.01).astype(np.float32)
+    C, D = orc.gemm_blockscaled(A, fa, sA, B, fb, sB, gb)
+    Ce, De = _exact_gemm(orc, A, fa, sA, B, fb, sB, gb)
+    assert np.all(np.abs(C - Ce) <= 4 * 2.0 ** -52 * De)
+    assert np.allclose(D, De, rtol=1e-15, atol=0)
+    Cr, Dr = orc.gemm_blockscaled(A, fa, sA, B, fb, sB, gb, rows=np.array([1]))
+    assert np.array_equal(Cr[0], C[1]) and np.array_equal(Dr[0], D[1])
+
+
+def test_gemm_unit_scales_is_integer_matmul(orc):
+    """With unit scales and K = 128 the GEMM is an integer matmul (numpy int64)."""
+    rng = np.random.default_rng(8)
+    # E4M3 codes of the integers 1..16: 1.0 is 0x38; integers m in [8,16) sit at 0x50 + (m - 8)
+    ints = np.arange(-16, 17)
+    code = {0: 0x00}
+    for v in range(1, 17):
+        c = next(c for c in range(128) if orc.decode(c, E4) == v)
+        code[v], code[-v] = c, c | 0x80
+    Ai = rng.choice(ints, size=(8, 128))
+    Bi = rng.choice(ints, size=(128, 128))
+    A = np.vectorize(code.get)(Ai).astype(np.uint8)
+    B = np.vectorize(code.get)(Bi).astype(np.uint8)
+    C, _ = orc.gemm_blockscaled(A, E4, np.ones((8, 1), np.float32), B, E4, np.ones((1, 1), np.float32), 2)
+    assert np.array_equal(C, (Ai @ Bi.T).astype(np.float64))
+
+
+def test_gemm_identity_b(orc):
+    """B = identity codes (1.0 on the diagonal) with unit B scales returns dec(A) * sA."""
+    rng = np.random.default_rng(9)
+    M, K = 4, 256
+    A = _rand_codes(rng, (M, K), E4)
+    sA = (rng.random((M, 2)) + 0.5).astype(np.float32)
+    B = np.zeros((K, K), np.uint8)
+    B[np.arange(K), np.arange(K)] = 0x38
+    C, _ = orc.gemm_blockscaled(A, E4, sA, B, E4, np.ones((2, 2), np.float32), 2)
+    t = orc.decode_table(E4)
+    want = t[A] * np.repeat(sA.astype(np.float64), 128, axis=1)
+    assert np.array_equal(C, want)
+
+
+def test_rel_err_matches_numpy_norm(orc):
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((17, 33)).astype(np.float32)
+    y = x + rng.standard_normal((17, 33)).astype(np.float32) * 0.01
+    want = np.linalg.norm(y.astype(np.float64) - x.astype(np.float64)) / np.linalg.norm(x.astype(np.float64))
+    assert abs(orc.rel_err(y, x) - want) < 1e-14
