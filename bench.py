@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the FP8 quantize + block-scaled GEMM hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic input:
+  1. a delayed-scaling step on bf16 8192x8192 tensors: the activation copy
+     x_t (sigma_t * N(0,1), sigma_t log-uniform in [0.5, 50]) quantized to
+     E4M3FN and the gradient copy g_t (|g| log-uniform in [1e-6, 1e-2])
+     quantized to E5M2, each with the scale of the previous steps (window
+     16) and the amax fused into the same pass, the x_t codes dequantized
+     back to bf16, then both scalers updated;
+  2. the LLM-layer fused path: bf16 activations 16384x7168 (N(0,1), four
+     outlier columns x1e3) quantized 1x128 to E4M3FN, times the E4M3FN
+     weight 18432x7168 with 128x128 scales (quantized once, untimed), fp32
+     accumulation promoted every 128 K, bf16 output.
+Inputs rotate over several buffers so repeated reads are not served from
+the 256 MB last-level cache.
+
+`value` is the step's throughput in TFLOP/s: the layer GEMM's 2*M*N*K per
+step over the step time.  Per-kernel figures (GB/s for the quantizers,
+TFLOP/s for the GEMM, each with its roofline fraction) are measured with
+events around each launch on the launch stream.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step and extrapolates per unit.
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0      # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+
+# workload sizes
+DS_ROWS = DS_COLS = 8192        # delayed-scaling tensors
+LM, LN, LK = 16384, 18432, 7168  # LLM layer: X [M,K] bf16, W [N,K], C [M,N] bf16
+WINDOW = 16
+N_ROT = 8                        # rotating delayed-scaling buffers per tensor
+X_ROT = 2
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic():
+    n = DS_ROWS * DS_COLS
+    nx = LM * LK
+    return {
+        "quantize_tensor_bytes": n * 2 + n + 4,            # bf16 read, codes written, amax
+        "dequantize_bytes": n + 2 * n + 4,                  # codes read, bf16 written, scale
+        "quantize_1x128_bytes": nx * 2 + nx + 4 * nx // 128,  # bf16 read, codes + scales written
+        "gemm_flop": 2 * LM * LN * LK,
+    }
+
+
+def run_gpu(steps: int, warmup: int):
+    import torch
+
+    import block_scaled_precision_amax_amd as fq
+    from block_scaled_precision_amax_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n = DS_ROWS * DS_COLS
+    log("building inputs ...")
+    sig = W.sigma_schedule(64, seed=2)
+    xs = [W.delayed_step(DS_ROWS, DS_COLS, sig[i], seed=200 + i, device=dev) for i in range(N_ROT)]
+    gs = [W.gradient(DS_ROWS, DS_COLS, seed=300 + i, device=dev, dtype=torch.bfloat16) for i in range(N_ROT)]
+    Xs = [W.activation(LM, LK, seed=4 + 10 * i, factor=1e3, dtype=torch.bfloat16, device=dev) for i in range(X_ROT)]
+    w32 = W.weight(LN, LK, seed=40, device=dev)
+    qW = torch.empty(LN, LK, dtype=torch.uint8, device=dev)
+    sW = torch.empty(LN // 128, LK // 128, dtype=torch.float32, device=dev)
+    fq.fp8q_quantize_128x128(w32, LN, LK, LK, fq.E4M3FN, 1e-12, qW, LK, sW, LK // 128)
+    del w32
+    qx = torch.empty(n, dtype=torch.uint8, device=dev)
+    qg = torch.empty(n, dtype=torch.uint8, device=dev)
+    xhat = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    qX = torch.empty(LM, LK, dtype=torch.uint8, device=dev)
+    sX = torch.empty(LM, LK // 128, dtype=torch.float32, device=dev)
+    C = torch.empty(LM, LN, dtype=torch.bfloat16, device=dev)
+    st_x = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
+    st_g = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
+    am_x = torch.zeros(1, dtype=torch.float32, device=dev)
+    am_g = torch.zeros(1, dtype=torch.float32, device=dev)
+    fq.fp8q_delayed_scaler_init(st_x, WINDOW, 448.0, 1e-12, 1.0)
+    fq.fp8q_delayed_scaler_init(st_g, WINDOW, 57344.0, 1e-12, 1.0)
+    sc_x = st_x.data_ptr() + fq.SCALER_SCALE_OFFSET
+    sc_g = st_g.data_ptr() + fq.SCALER_SCALE_OFFSET
+    torch.cuda.synchronize()
+
+    names = ["quantize_tensor_x", "quantize_tensor_g", "dequantize_x", "scaler_updates", "quantize_1x128",
+             "gemm"]
+    ev = {k: [] for k in names}
+
+    def E():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def step(t: int, timed: bool):
+        x, g, X = xs[t % N_ROT], gs[t % N_ROT], Xs[t % X_ROT]
+        marks = [E()] if timed else None
+        fq.fp8q_quantize_tensor(x, n, fq.E4M3FN, sc_x, qx, am_x)
+        if timed: marks.append(E())
+        fq.fp8q_quantize_tensor(g, n, fq.E5M2, sc_g, qg, am_g)
+        if timed: marks.append(E())
+        fq.fp8q_dequantize(qx, fq.E4M3FN, 1, n, n, sc_x, fq.GRAN_TENSOR, 1, xhat, n)
+        if timed: marks.append(E())
+        fq.fp8q_delayed_scaler_update(st_x, am_x)
+        fq.fp8q_delayed_scaler_update(st_g, am_g)
+        if timed: marks.append(E())
+        fq.fp8q_quantize_1x128(X, LM, LK, LK, fq.E4M3FN, 1e-12, qX, LK, sX, LK // 128)
+        if timed: marks.append(E())
+        fq.fp8q_gemm_blockscaled(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW, fq.GRAN_128x128,
+                                 LK // 128, 1, C, LN, LM, LN, LK)
+        if timed:
+            marks.append(E())
+            for k, a, b in zip(names, marks[:-1], marks[1:]):
+                ev[k].append((a, b))
+
+    log(f"warmup {warmup} steps ...")
+    for t in range(warmup):
+        step(t, False)
+    torch.cuda.synchronize()
+    log(f"timing {steps} steps ...")
+    t0 = time.perf_counter()
+    for t in range(warmup, warmup + steps):
+        step(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in ev.items()}
+    first = ev[names[0]][0][0]
+    last = ev[names[-1]][-1][1]
+    gpu_ms = first.elapsed_time(last) / steps
+    inputs = {"ds": (xs[0], gs[0]), "X": Xs[0], "qW": qW, "sW": sW}
+    return per, gpu_ms, wall * 1e3 / steps, inputs
+
+
+def cpu_baseline(inputs, budget_s: float = 20.0):
+    """The CPU oracle (as it stands) on a bounded sample of the step, rates
+    extrapolated per element / per MAC to the full step."""
+    import numpy as np
+    import torch
+
+    import oracle as orc
+    from block_scaled_precision_amax_amd import workloads as W
+
+    orc.build(force=False)
+    alg = algorithmic()
+    n = DS_ROWS * DS_COLS
+    x, g = inputs["ds"]
+    rows_ds = 512
+    xs = W.to_numpy_input(x[:rows_ds])
+    gs = W.to_numpy_input(g[:rows_ds])
+    m_ds = rows_ds * DS_COLS
+    t0 = time.perf_counter()
+    qx = orc.quantize_tensor(xs, orc.E4M3FN, 0.05)
+    orc.quantize_tensor(gs, orc.E5M2, 1e-6)
+    orc.amax(xs)
+    orc.amax(gs)
+    orc.dequantize(qx.reshape(1, -1), orc.E4M3FN, np.array([0.05], np.float32), orc.GRAN_TENSOR, out_bf16=True)
+    t_ds = time.perf_counter() - t0
+    rows_x = 256
+    Xs = W.to_numpy_input(inputs["X"][:rows_x])
+    t0 = time.perf_counter()
+    qa, sa = orc.quantize_1x128(Xs, orc.E4M3FN)
+    t_q = time.perf_counter() - t0
+    qW = inputs["qW"].cpu().numpy()
+    sW = inputs["sW"].cpu().numpy()
+    rows_g = 1
+    t0 = time.perf_counter()
+    orc.gemm_blockscaled(qa[:rows_g], orc.E4M3FN, sa[:rows_g], qW, orc.E4M3FN, sW, orc.GRAN_128x128)
+    t_g1 = time.perf_counter() - t0
+    # grow the GEMM sample to use the rest of the budget
+    spare = max(budget_s - (t_ds + t_q + t_g1), 0.0)
+    rows_g2 = int(min(max(spare / max(t_g1, 1e-3), 1), rows_x - 1))
+    t0 = time.perf_counter()
+    orc.gemm_blockscaled(qa[1:1 + rows_g2], orc.E4M3FN, sa[1:1 + rows_g2], qW, orc.E4M3FN, sW,
+                         orc.GRAN_128x128)
+    t_g = time.perf_counter() - t0
+    rows_g2 = max(rows_g2, 1)
+    est = (t_ds * n / m_ds + t_q * LM / rows_x + t_g * LM / rows_g2)
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {
+        "value": alg["gemm_flop"] / est / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"oracle on {rows_ds} of {DS_ROWS} rows of both delayed-scaling tensors (quantize, amax, "
+                   f"dequantize), {rows_x} of {LM} activation rows (1x128 quantize) and {rows_g2} of {LM} "
+                   f"GEMM rows; measured {t_ds + t_q + t_g + t_g1:.1f} s, extrapolated per element / per row "
+                   f"to a full step of {est:.1f} s"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    per, gpu_ms, wall_ms, inputs = run_gpu(args.steps, args.warmup)
+    alg = algorithmic()
+    step_ms = max(gpu_ms, wall_ms)
+    value = alg["gemm_flop"] / (step_ms * 1e-3) / 1e12
+
+    def gbps(bytes_, ms):
+        return bytes_ / (ms * 1e-3) / 1e9
+
+    gemm_tflops = alg["gemm_flop"] / (per["gemm"] * 1e-3) / 1e12
+    q_t = gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_x"])
+    q_g = gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_g"])
+    q_1 = gbps(alg["quantize_1x128_bytes"], per["quantize_1x128"])
+    dq = gbps(alg["dequantize_bytes"], per["dequantize_x"])
+    out = {
+        "metric": "quantize GB/s + block-scaled FP8 GEMM TFLOPS, % of HBM / FP8-MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3fn/e5m2 codes, fp32 accumulate",
+        "data": "synthetic (seeded torch generators)",
+        "config": {
+            "workload": ("fp8 hot path step: delayed-scaling quantize of bf16 8192x8192 x (E4M3FN) and g (E5M2) "
+                         "with fused amax, window 16, x dequantized to bf16; LLM layer bf16 X 16384x7168 1x128 "
+                         "E4M3FN quantize + block-scaled GEMM vs E4M3FN W 18432x7168 (128x128 scales), bf16 out"),
+            "M": LM, "N": LN, "K": LK, "delayed_shape": [DS_ROWS, DS_COLS], "window": WINDOW,
+        },
+        "roofline": {
+            "bound": "mfma", "kernel": "gemm_blockscaled",
+            "achieved": round(gemm_tflops, 2), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None,
+        },
+        "kernels": {
+            "gemm_blockscaled": {"ms": round(per["gemm"], 4), "TFLOP/s": round(gemm_tflops, 2),
+                                 "frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4)},
+            "quantize_1x128_bf16": {"ms": round(per["quantize_1x128"], 4), "GB/s": round(q_1, 1),
+                                    "frac_hbm": round(q_1 / HBM_PEAK_GBPS, 4)},
+            "quantize_tensor_bf16_e4m3": {"ms": round(per["quantize_tensor_x"], 4), "GB/s": round(q_t, 1),
+                                          "frac_hbm": round(q_t / HBM_PEAK_GBPS, 4)},
+            "quantize_tensor_bf16_e5m2": {"ms": round(per["quantize_tensor_g"], 4), "GB/s": round(q_g, 1),
+                                          "frac_hbm": round(q_g / HBM_PEAK_GBPS, 4)},
+            "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
+                                "frac_hbm": round(dq / HBM_PEAK_GBPS, 4)},
+            "scaler_update_x2": {"ms": round(per["scaler_updates"], 4)},
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

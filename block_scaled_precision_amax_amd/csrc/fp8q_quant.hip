@@ -1,0 +1,607 @@
+// Amax-scaled FP8 quantizers for gfx950: amax, per-tensor (delayed) with a
+// fused running amax, fine-grained 1x128 and 128x128, the delayed scaler
+// and dequantization.
+//
+// What is computed follows the handbook chapter "混合精度与 FP8 训练",
+// section "FP8 训练" (quant / per_tensor / per_block) and the PyTorch-native
+// FP8 article (m.nxbn.cn/news/137885), sections 1.2-1.3 (formats) and
+// 4.1-4.3 (amax, scale factors, DelayedScaler, margin).  Every code and
+// scale is the one the IEEE definition q = enc(fl32(x / s)),
+// s = fl32(max(amax, eps) / MAX) gives; see fp8q_internal.h for the
+// division and the cast.
+//
+// All of these kernels are HBM-bound streams: 16-byte loads with lanes
+// on consecutive addresses, the reductions in registers and DPP, codes
+// packed four to a dword by the hardware conversion.
+#include "fp8q_internal.h"
+
+namespace fp8q {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+static constexpr int kThreads = 256;
+
+// Largest |bf16| bit pattern of a dword pair, by a packed 16-bit max.
+__device__ __forceinline__ uint32_t pk_absmax(uint32_t acc, uint32_t v) {
+  u16x2 a = __builtin_bit_cast(u16x2, acc);
+  u16x2 b = __builtin_bit_cast(u16x2, v & 0x7FFF7FFFu);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+// Fold the two halves of a packed bf16 max into an fp32 abs bit pattern.
+__device__ __forceinline__ uint32_t pk_fold(uint32_t acc) {
+  return max(acc & 0xFFFFu, acc >> 16) << 16;
+}
+
+// Workgroup-wide maximum of one value per thread (kThreads threads).
+__device__ __forceinline__ uint32_t block_max(uint32_t v) {
+  __shared__ uint32_t part[kThreads / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t m = part[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) m = max(m, part[i]);
+  __syncthreads();
+  return m;
+}
+
+__global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
+
+// ---------------------------------------------------------------- amax
+// One read of x; per-thread max of |x| bit patterns, then one atomic max
+// per workgroup on the fp32 pattern (non-negative floats order like their
+// bit patterns, so the result does not depend on the order).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t n,
+                                                   uint32_t* __restrict__ out) {
+  const int64_t per_vec = DT == FP8Q_F32 ? 4 : 8;
+  const int64_t nvec = n / per_vec;
+  const u32x4* xv = (const u32x4*)x;
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(xv + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if constexpr (DT == FP8Q_F32) {
+        m = max(m, max(v[u].x & 0x7FFFFFFFu, v[u].y & 0x7FFFFFFFu));
+        m = max(m, max(v[u].z & 0x7FFFFFFFu, v[u].w & 0x7FFFFFFFu));
+      } else {
+        m = pk_absmax(m, v[u].x);
+        m = pk_absmax(m, v[u].y);
+        m = pk_absmax(m, v[u].z);
+        m = pk_absmax(m, v[u].w);
+      }
+    }
+  }
+  for (; i < nvec; i += stride) {
+    u32x4 v = __builtin_nontemporal_load(xv + i);
+    if constexpr (DT == FP8Q_F32) {
+      m = max(m, max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu));
+      m = max(m, max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+    } else {
+      m = pk_absmax(m, v.x);
+      m = pk_absmax(m, v.y);
+      m = pk_absmax(m, v.z);
+      m = pk_absmax(m, v.w);
+    }
+  }
+  if constexpr (DT == FP8Q_BF16) m = pk_fold(m);
+  // tail elements (n not a multiple of the vector width)
+  if (blockIdx.x == 0) {
+    for (int64_t j = nvec * per_vec + threadIdx.x; j < n; j += kThreads) {
+      uint32_t b = DT == FP8Q_F32 ? ((const uint32_t*)x)[j]
+                                  : (uint32_t)((const uint16_t*)x)[j] << 16;
+      m = max(m, b & 0x7FFFFFFFu);
+    }
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) atomicMax(out, canon_abs_bits(m));
+}
+
+// ---------------------------------------------------------------- per-tensor
+// Quantize with the scale at *scale (read on the device), folding max|x|
+// into *amax_acc when given.  The fast path divides with div_rn_wide; a
+// vector holding a NaN re-encodes its elements one by one (NaN -> 0x7F),
+// and a scale outside [2^-80, 2^80] (or NaN / zero / Inf) takes IEEE
+// division for every element.
+template <int DT, int FMT>
+__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float s, float r,
+                                           bool fast) {
+  if (fast)
+    return pack4<FMT>(sat<FMT>(div_rn_wide(a, s, r)), sat<FMT>(div_rn_wide(b, s, r)),
+                      sat<FMT>(div_rn_wide(c, s, r)), sat<FMT>(div_rn_wide(d, s, r)));
+  return enc1<FMT>(a / s) | (enc1<FMT>(b / s) << 8) | (enc1<FMT>(c / s) << 16) |
+         (enc1<FMT>(d / s) << 24);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t quant4_exact(float a, float b, float c, float d, float s) {
+  return enc1<FMT>(a / s) | (enc1<FMT>(b / s) << 8) | (enc1<FMT>(c / s) << 16) |
+         (enc1<FMT>(d / s) << 24);
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restrict__ x, int64_t n,
+                                                           const float* __restrict__ scale,
+                                                           uint8_t* __restrict__ q,
+                                                           uint32_t* __restrict__ amax_acc) {
+  const float s = *scale;
+  const bool fast = scale_ok(s);
+  const float r = 1.0f / s;
+  const int64_t per_vec = DT == FP8Q_F32 ? 4 : 8;
+  const int64_t nvec = n / per_vec;
+  const u32x4* xv = (const u32x4*)x;
+  uint32_t m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nvec; i0 += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (i0 + u * stride < nvec) v[u] = __builtin_nontemporal_load(xv + i0 + u * stride);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t i = i0 + u * stride;
+      if (i >= nvec) break;
+      if constexpr (DT == FP8Q_F32) {
+        uint32_t mv = max(max(v[u].x & 0x7FFFFFFFu, v[u].y & 0x7FFFFFFFu),
+                          max(v[u].z & 0x7FFFFFFFu, v[u].w & 0x7FFFFFFFu));
+        m = max(m, mv);
+        float a = __uint_as_float(v[u].x), b = __uint_as_float(v[u].y);
+        float c = __uint_as_float(v[u].z), d = __uint_as_float(v[u].w);
+        uint32_t w = quant4<DT, FMT>(a, b, c, d, s, r, fast);
+        if (mv > 0x7F800000u) w = quant4_exact<FMT>(a, b, c, d, s);
+        __builtin_nontemporal_store(w, (uint32_t*)q + i);
+      } else {
+        uint32_t pm = pk_absmax(pk_absmax(0u, v[u].x), v[u].y);
+        pm = pk_absmax(pk_absmax(pm, v[u].z), v[u].w);
+        uint32_t mv = pk_fold(pm);
+        m = max(m, mv);
+        float e0 = bf_lo(v[u].x), e1 = bf_hi(v[u].x), e2 = bf_lo(v[u].y), e3 = bf_hi(v[u].y);
+        float e4 = bf_lo(v[u].z), e5 = bf_hi(v[u].z), e6 = bf_lo(v[u].w), e7 = bf_hi(v[u].w);
+        u32x2 w;
+        w.x = quant4<DT, FMT>(e0, e1, e2, e3, s, r, fast);
+        w.y = quant4<DT, FMT>(e4, e5, e6, e7, s, r, fast);
+        if (mv > 0x7F800000u) {
+          w.x = quant4_exact<FMT>(e0, e1, e2, e3, s);
+          w.y = quant4_exact<FMT>(e4, e5, e6, e7, s);
+        }
+        __builtin_nontemporal_store(w, (u32x2*)q + i);
+      }
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t j = nvec * per_vec + threadIdx.x; j < n; j += kThreads) {
+      uint32_t b = DT == FP8Q_F32 ? ((const uint32_t*)x)[j]
+                                  : (uint32_t)((const uint16_t*)x)[j] << 16;
+      m = max(m, b & 0x7FFFFFFFu);
+      q[j] = (uint8_t)enc1<FMT>(__uint_as_float(b) / s);
+    }
+  }
+  if (amax_acc) {
+    m = block_max(m);
+    if (threadIdx.x == 0) atomicMax(amax_acc, canon_abs_bits(m));
+  }
+}
+
+// ---------------------------------------------------------------- 1x128
+// Each 16-lane DPP row of a wavefront owns one 128-element block: 16 lanes
+// x 16 bytes is the whole block for bf16, and two such loads for fp32
+// (element offsets 4l and 64+4l).  A wavefront walks groups of four
+// consecutive blocks; each lane keeps kGroups groups in flight.
+static constexpr int kGroups = 4;
+
+template <int DT, int FMT>
+__device__ __forceinline__ void quant_block_regs(const u32x4* v, uint32_t amax_bits, float eps,
+                                                 uint8_t* qrow, float* sptr, int l) {
+  // v[0] (and v[1] for fp32) hold this lane's 8 elements of the block.
+  const float amax = __uint_as_float(canon_abs_bits(amax_bits));
+  const float s = block_scale<FMT>(amax, eps);
+  if (l == 0) *sptr = s;
+  if (scale_ok(s)) {
+    const float r = 1.0f / s;
+    if constexpr (DT == FP8Q_F32) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w = pack4<FMT>(sat<FMT>(div_rn(__uint_as_float(v[h].x), s, r)),
+                                sat<FMT>(div_rn(__uint_as_float(v[h].y), s, r)),
+                                sat<FMT>(div_rn(__uint_as_float(v[h].z), s, r)),
+                                sat<FMT>(div_rn(__uint_as_float(v[h].w), s, r)));
+        __builtin_nontemporal_store(w, (uint32_t*)(qrow + 4 * l + 64 * h));
+      }
+    } else {
+      u32x2 w;
+      w.x = pack4<FMT>(sat<FMT>(div_rn(bf_lo(v[0].x), s, r)), sat<FMT>(div_rn(bf_hi(v[0].x), s, r)),
+                       sat<FMT>(div_rn(bf_lo(v[0].y), s, r)), sat<FMT>(div_rn(bf_hi(v[0].y), s, r)));
+      w.y = pack4<FMT>(sat<FMT>(div_rn(bf_lo(v[0].z), s, r)), sat<FMT>(div_rn(bf_hi(v[0].z), s, r)),
+                       sat<FMT>(div_rn(bf_lo(v[0].w), s, r)), sat<FMT>(div_rn(bf_hi(v[0].w), s, r)));
+      __builtin_nontemporal_store(w, (u32x2*)(qrow + 8 * l));
+    }
+  } else {
+    if constexpr (DT == FP8Q_F32) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w = quant4_exact<FMT>(__uint_as_float(v[h].x), __uint_as_float(v[h].y),
+                                       __uint_as_float(v[h].z), __uint_as_float(v[h].w), s);
+        *(uint32_t*)(qrow + 4 * l + 64 * h) = w;
+      }
+    } else {
+      u32x2 w;
+      w.x = quant4_exact<FMT>(bf_lo(v[0].x), bf_hi(v[0].x), bf_lo(v[0].y), bf_hi(v[0].y), s);
+      w.y = quant4_exact<FMT>(bf_lo(v[0].z), bf_hi(v[0].z), bf_lo(v[0].w), bf_hi(v[0].w), s);
+      *(u32x2*)(qrow + 8 * l) = w;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t lane_absmax(const u32x4* v) {
+  if constexpr (DT == FP8Q_F32) {
+    uint32_t m = max(max(v[0].x & 0x7FFFFFFFu, v[0].y & 0x7FFFFFFFu),
+                     max(v[0].z & 0x7FFFFFFFu, v[0].w & 0x7FFFFFFFu));
+    uint32_t m2 = max(max(v[1].x & 0x7FFFFFFFu, v[1].y & 0x7FFFFFFFu),
+                      max(v[1].z & 0x7FFFFFFFu, v[1].w & 0x7FFFFFFFu));
+    return max(m, m2);
+  } else {
+    uint32_t pm = pk_absmax(pk_absmax(0u, v[0].x), v[0].y);
+    pm = pk_absmax(pk_absmax(pm, v[0].z), v[0].w);
+    return pk_fold(pm);
+  }
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict__ x, int64_t nkb,
+                                                          int64_t nblocks, int64_t ldx, float eps,
+                                                          uint8_t* __restrict__ q, int64_t ldq,
+                                                          float* __restrict__ scales, int64_t ld_s) {
+  constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
+  constexpr int NV = DT == FP8Q_F32 ? 2 : 1;  // 16-byte vectors per lane per block
+  const int lane = threadIdx.x & 63;
+  const int w = lane >> 4, l = lane & 15;
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const char* xb = (const char*)x;
+  for (int64_t b0 = wave * 4 * kGroups; b0 < nblocks; b0 += nwaves * 4 * kGroups) {
+    u32x4 v[kGroups][NV];
+    int64_t row[kGroups], kb[kGroups];
+    bool ok[kGroups];
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const int64_t bg = b0 + 4 * g;  // wave-uniform
+      int64_t r0 = bg / nkb, k0 = bg - r0 * nkb + w;
+      while (k0 >= nkb) { k0 -= nkb; ++r0; }
+      row[g] = r0;
+      kb[g] = k0;
+      ok[g] = bg + w < nblocks;
+      if (ok[g]) {
+        const u32x4* p = (const u32x4*)(xb + (r0 * ldx + 128 * k0) * esz);
+#pragma unroll
+        for (int h = 0; h < NV; ++h) v[g][h] = __builtin_nontemporal_load(p + l + 16 * h);
+      } else {
+#pragma unroll
+        for (int h = 0; h < NV; ++h) v[g][h] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kGroups; ++g) {
+      const uint32_t am = row16_max(lane_absmax<DT>(v[g]));
+      if (ok[g])
+        quant_block_regs<DT, FMT>(v[g], am, eps, q + row[g] * ldq + 128 * kb[g],
+                                  scales + row[g] * ld_s + kb[g], l);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 128x128
+// One workgroup per 128x128 tile: the tile is read into registers once
+// (bf16: 8 rows x 16 B per thread; fp32: 16 rows x 16 B), its amax found
+// by a workgroup reduction, then quantized from the registers.
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_128x128(const void* __restrict__ x, int64_t nkb,
+                                                            int64_t ldx, float eps,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            float* __restrict__ scales,
+                                                            int64_t ld_s) {
+  constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
+  constexpr int LPR = DT == FP8Q_F32 ? 32 : 16;  // lanes per 128-element row
+  constexpr int RSTEP = kThreads / LPR;           // rows covered by one pass
+  constexpr int NR = 128 / RSTEP;                 // passes
+  const int64_t rb = blockIdx.x / nkb, kb = blockIdx.x - rb * nkb;
+  const int c = threadIdx.x % LPR, r0 = threadIdx.x / LPR;
+  const char* base = (const char*)x + ((rb * 128 + r0) * ldx + kb * 128) * esz;
+  u32x4 v[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i)
+    v[i] = __builtin_nontemporal_load((const u32x4*)(base + (int64_t)i * RSTEP * ldx * esz) + c);
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    if constexpr (DT == FP8Q_F32) {
+      m = max(m, max(max(v[i].x & 0x7FFFFFFFu, v[i].y & 0x7FFFFFFFu),
+                     max(v[i].z & 0x7FFFFFFFu, v[i].w & 0x7FFFFFFFu)));
+    } else {
+      m = pk_absmax(pk_absmax(m, v[i].x), v[i].y);
+      m = pk_absmax(pk_absmax(m, v[i].z), v[i].w);
+    }
+  }
+  if constexpr (DT == FP8Q_BF16) m = pk_fold(m);
+  m = block_max(m);
+  const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
+  if (threadIdx.x == 0) scales[rb * ld_s + kb] = s;
+  uint8_t* qb = q + (rb * 128 + r0) * ldq + kb * 128;
+  const bool fast = scale_ok(s);
+  const float r = 1.0f / s;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    uint8_t* qr = qb + (int64_t)i * RSTEP * ldq;
+    if constexpr (DT == FP8Q_F32) {
+      float a = __uint_as_float(v[i].x), b = __uint_as_float(v[i].y);
+      float cc = __uint_as_float(v[i].z), d = __uint_as_float(v[i].w);
+      uint32_t w = fast ? pack4<FMT>(sat<FMT>(div_rn(a, s, r)), sat<FMT>(div_rn(b, s, r)),
+                                     sat<FMT>(div_rn(cc, s, r)), sat<FMT>(div_rn(d, s, r)))
+                        : quant4_exact<FMT>(a, b, cc, d, s);
+      __builtin_nontemporal_store(w, (uint32_t*)(qr + 4 * c));
+    } else {
+      float e[8] = {bf_lo(v[i].x), bf_hi(v[i].x), bf_lo(v[i].y), bf_hi(v[i].y),
+                    bf_lo(v[i].z), bf_hi(v[i].z), bf_lo(v[i].w), bf_hi(v[i].w)};
+      u32x2 w;
+      if (fast) {
+        w.x = pack4<FMT>(sat<FMT>(div_rn(e[0], s, r)), sat<FMT>(div_rn(e[1], s, r)),
+                         sat<FMT>(div_rn(e[2], s, r)), sat<FMT>(div_rn(e[3], s, r)));
+        w.y = pack4<FMT>(sat<FMT>(div_rn(e[4], s, r)), sat<FMT>(div_rn(e[5], s, r)),
+                         sat<FMT>(div_rn(e[6], s, r)), sat<FMT>(div_rn(e[7], s, r)));
+      } else {
+        w.x = quant4_exact<FMT>(e[0], e[1], e[2], e[3], s);
+        w.y = quant4_exact<FMT>(e[4], e[5], e[6], e[7], s);
+      }
+      __builtin_nontemporal_store(w, (u32x2*)(qr + 8 * c));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- scaler
+__global__ void k_scaler_init(fp8q_scaler* st, int32_t window, float max_val, float eps,
+                              float margin) {
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) st->ring[i] = 0.0f;
+  if (threadIdx.x == 0) {
+    st->window = window;
+    st->count = 0;
+    st->pos = 0;
+    st->max_val = max_val;
+    st->eps = eps;
+    st->margin = margin;
+    st->scale = 1.0f;
+  }
+}
+
+// One wavefront: push the amax, then (window full) the window maximum with
+// NaN winning, then the scale.  The PyTorch-native FP8 article, section
+// 4.2: the amax of earlier steps sets the scale of the next one, and the
+// scale is only recomputed once the window holds `window` values.
+// Contribution of one history entry to the window maximum: NaN wins,
+// values <= 0 contribute nothing (the maximum starts from 0).
+__device__ __forceinline__ uint32_t hist_bits(float f) {
+  if (f != f) return 0x7FC00000u;
+  return f > 0.0f ? __float_as_uint(f) : 0u;
+}
+
+__global__ __launch_bounds__(64) void k_scaler_update(fp8q_scaler* st, uint32_t* amax) {
+  const int lane = threadIdx.x;
+  float a = __uint_as_float(*amax);
+  if (a != a) a = __uint_as_float(0x7FC00000u);
+  const int32_t window = st->window, pos = st->pos;
+  int32_t count = st->count;
+  __syncthreads();
+  if (lane == 0) {
+    *amax = 0u;  // consumed: ready to accumulate the next step
+    st->ring[pos] = a;
+    st->pos = pos + 1 == window ? 0 : pos + 1;
+    st->count = count < window ? count + 1 : count;
+  }
+  count = count < window ? count + 1 : count;
+  __syncthreads();
+  if (count >= window) {
+    uint32_t m = 0;
+    for (int i = lane; i < window; i += 64) m = max(m, hist_bits(i == pos ? a : st->ring[i]));
+    m = wave_max(m);
+    if (lane == 0) {
+      const float wmax = __uint_as_float(m);
+      const float mm = (wmax < st->eps) ? st->eps : wmax;  // NaN stays NaN
+      const float t = mm * st->margin;
+      st->scale = t / st->max_val;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dequantize
+template <int FMT>
+__device__ __forceinline__ float2 dec2(uint32_t w, bool hi) {
+  if constexpr (FMT == FP8Q_E4M3FN) {
+    auto t = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    return make_float2(t[0], t[1]);
+  } else {
+    auto t = hi ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    return make_float2(t[0], t[1]);
+  }
+}
+
+__device__ __forceinline__ float canon_nan(float f) {
+  return f != f ? __uint_as_float(0x7FC00000u) : f;
+}
+
+// Work unit: (row, 4096-column chunk); each thread handles 4 groups of 4
+// codes (one dword load; one 16-byte fp32 or 8-byte bf16 store each).
+template <int FMT, int GRAN, int ODT>
+__global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ q, int64_t rows,
+                                                      int64_t cols, int64_t ldq,
+                                                      const float* __restrict__ scales,
+                                                      int64_t ld_s, void* __restrict__ y,
+                                                      int64_t ldy) {
+  const int64_t nchunk = (cols + 4095) / 4096;
+  const int64_t units = rows * nchunk;
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t r = u / nchunk, ch = u - r * nchunk;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int64_t c = ch * 4096 + g * 1024 + 4 * threadIdx.x;
+      if (c >= cols) break;
+      float s;
+      if constexpr (GRAN == FP8Q_GRAN_TENSOR) s = scales[0];
+      else if constexpr (GRAN == FP8Q_GRAN_1x128) s = scales[r * ld_s + (c >> 7)];
+      else s = scales[(r >> 7) * ld_s + (c >> 7)];
+      const uint8_t* qp = q + r * ldq + c;
+      if (c + 4 <= cols) {
+        const uint32_t w = __builtin_nontemporal_load((const uint32_t*)qp);
+        const float2 lo = dec2<FMT>(w, false), hi = dec2<FMT>(w, true);
+        const float o0 = canon_nan(lo.x * s), o1 = canon_nan(lo.y * s);
+        const float o2 = canon_nan(hi.x * s), o3 = canon_nan(hi.y * s);
+        if constexpr (ODT == FP8Q_F32) {
+          u32x4 o = {__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+          __builtin_nontemporal_store(o, (u32x4*)((float*)y + r * ldy + c));
+        } else {
+          u32x2 o;
+          o.x = f32_to_bf16(o0) | (f32_to_bf16(o1) << 16);
+          o.y = f32_to_bf16(o2) | (f32_to_bf16(o3) << 16);
+          __builtin_nontemporal_store(o, (u32x2*)((uint16_t*)y + r * ldy + c));
+        }
+      } else {
+        for (int64_t j = c; j < cols; ++j) {
+          const float o = canon_nan(dec2<FMT>(q[r * ldq + j], false).x * s);
+          if constexpr (ODT == FP8Q_F32) ((float*)y)[r * ldy + j] = o;
+          else ((uint16_t*)y)[r * ldy + j] = (uint16_t)f32_to_bf16(o);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- launches
+static int grid_for(int64_t work_items, int per_cu) {
+  const int64_t cap = (int64_t)device_cu_count() * per_cu;
+  int64_t g = (work_items + kThreads - 1) / kThreads;
+  if (g > cap) g = cap;
+  return g < 1 ? 1 : (int)g;
+}
+
+int launch_amax(const void* x, int dt, int64_t n, float* amax, hipStream_t st) {
+  hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, st, (uint32_t*)amax, 0u);
+  if (int e = check_launch("amax reset")) return e;
+  const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
+  const int grid = grid_for(nvec / 4, 8);
+  if (dt == FP8Q_F32)
+    hipLaunchKernelGGL(k_amax<FP8Q_F32>, dim3(grid), dim3(kThreads), 0, st, x, n, (uint32_t*)amax);
+  else
+    hipLaunchKernelGGL(k_amax<FP8Q_BF16>, dim3(grid), dim3(kThreads), 0, st, x, n, (uint32_t*)amax);
+  return check_launch("amax");
+}
+
+template <int DT, int FMT>
+static void launch_qt(int grid, const void* x, int64_t n, const float* scale, uint8_t* q,
+                      float* amax_acc, hipStream_t st) {
+  hipLaunchKernelGGL((k_quant_tensor<DT, FMT>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+                     (uint32_t*)amax_acc);
+}
+
+int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const float* scale, uint8_t* q,
+                           float* amax_acc, hipStream_t st) {
+  const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
+  const int grid = grid_for(nvec / 4, 8);
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st);
+  else if (dt == FP8Q_F32) launch_qt<FP8Q_F32, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st);
+  else if (fmt == FP8Q_E4M3FN) launch_qt<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st);
+  else launch_qt<FP8Q_BF16, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st);
+  return check_launch("quantize_tensor");
+}
+
+template <int DT, int FMT>
+static void launch_q1(int grid, const void* x, int64_t nkb, int64_t nblocks, int64_t ldx, float eps,
+                      uint8_t* q, int64_t ldq, float* scales, int64_t ld_s, hipStream_t st) {
+  hipLaunchKernelGGL((k_quant_1x128<DT, FMT>), dim3(grid), dim3(kThreads), 0, st, x, nkb, nblocks, ldx,
+                     eps, q, ldq, scales, ld_s);
+}
+
+int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                          float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                          hipStream_t st) {
+  const int64_t nkb = cols / 128, nblocks = rows * nkb;
+  // one wavefront handles 4*kGroups blocks per pass
+  const int64_t waves = (nblocks + 4 * kGroups - 1) / (4 * kGroups);
+  const int grid = grid_for(waves * 64, 8);
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1<FP8Q_F32, FP8Q_E4M3FN>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (dt == FP8Q_F32) launch_q1<FP8Q_F32, FP8Q_E5M2>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (fmt == FP8Q_E4M3FN) launch_q1<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
+  else launch_q1<FP8Q_BF16, FP8Q_E5M2>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
+  return check_launch("quantize_1x128");
+}
+
+template <int DT, int FMT>
+static void launch_q128(int64_t tiles, const void* x, int64_t nkb, int64_t ldx, float eps, uint8_t* q,
+                        int64_t ldq, float* scales, int64_t ld_s, hipStream_t st) {
+  hipLaunchKernelGGL((k_quant_128x128<DT, FMT>), dim3((unsigned)tiles), dim3(kThreads), 0, st, x, nkb,
+                     ldx, eps, q, ldq, scales, ld_s);
+}
+
+int launch_quantize_128x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                            float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                            hipStream_t st) {
+  const int64_t nkb = cols / 128, tiles = (rows / 128) * nkb;
+  if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "quantize_128x128: more than 2^31-1 tiles");
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q128<FP8Q_F32, FP8Q_E4M3FN>(tiles, x, nkb, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (dt == FP8Q_F32) launch_q128<FP8Q_F32, FP8Q_E5M2>(tiles, x, nkb, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (fmt == FP8Q_E4M3FN) launch_q128<FP8Q_BF16, FP8Q_E4M3FN>(tiles, x, nkb, ldx, eps, q, ldq, scales, ld_s, st);
+  else launch_q128<FP8Q_BF16, FP8Q_E5M2>(tiles, x, nkb, ldx, eps, q, ldq, scales, ld_s, st);
+  return check_launch("quantize_128x128");
+}
+
+int launch_scaler_init(fp8q_scaler* s, int32_t window, float max_val, float eps, float margin,
+                       hipStream_t st) {
+  hipLaunchKernelGGL(k_scaler_init, dim3(1), dim3(256), 0, st, s, window, max_val, eps, margin);
+  return check_launch("delayed_scaler_init");
+}
+
+int launch_scaler_update(fp8q_scaler* s, float* amax, hipStream_t st) {
+  hipLaunchKernelGGL(k_scaler_update, dim3(1), dim3(64), 0, st, s, (uint32_t*)amax);
+  return check_launch("delayed_scaler_update");
+}
+
+template <int FMT, int GRAN, int ODT>
+static void launch_dq(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* scales,
+                      int64_t ld_s, void* y, int64_t ldy, hipStream_t st) {
+  const int64_t units = rows * ((cols + 4095) / 4096);
+  int64_t grid = units;
+  const int64_t cap = (int64_t)device_cu_count() * 16;
+  if (grid > cap) grid = cap;
+  hipLaunchKernelGGL((k_dequant<FMT, GRAN, ODT>), dim3((unsigned)grid), dim3(kThreads), 0, st, q, rows,
+                     cols, ldq, scales, ld_s, y, ldy);
+}
+
+template <int FMT, int GRAN>
+static void launch_dq_o(int out_dt, const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq,
+                        const float* scales, int64_t ld_s, void* y, int64_t ldy, hipStream_t st) {
+  if (out_dt == FP8Q_F32) launch_dq<FMT, GRAN, FP8Q_F32>(q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+  else launch_dq<FMT, GRAN, FP8Q_BF16>(q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+}
+
+template <int FMT>
+static void launch_dq_g(int gran, int out_dt, const uint8_t* q, int64_t rows, int64_t cols,
+                        int64_t ldq, const float* scales, int64_t ld_s, void* y, int64_t ldy,
+                        hipStream_t st) {
+  if (gran == FP8Q_GRAN_TENSOR) launch_dq_o<FMT, FP8Q_GRAN_TENSOR>(out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+  else if (gran == FP8Q_GRAN_1x128) launch_dq_o<FMT, FP8Q_GRAN_1x128>(out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+  else launch_dq_o<FMT, FP8Q_GRAN_128x128>(out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+}
+
+int launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
+                      const float* scales, int gran, int64_t ld_s, void* y, int out_dt, int64_t ldy,
+                      hipStream_t st) {
+  if (fmt == FP8Q_E4M3FN) launch_dq_g<FP8Q_E4M3FN>(gran, out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+  else launch_dq_g<FP8Q_E5M2>(gran, out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
+  return check_launch("dequantize");
+}
+
+}  // namespace fp8q

@@ -1,0 +1,194 @@
+/*
+ * fp8q.h -- C ABI of libfp8q.so: amax-scaled FP8 quantization and the
+ * block-scaled FP8 GEMM on AMD Instinct MI355X (gfx950).
+ *
+ * Sources cited below:
+ *   [A] the PyTorch-native FP8 article, m.nxbn.cn/news/137885 (its own
+ *       section numbers: 1.2 format table, 1.3 "FN" semantics, 3.1 FP8
+ *       linear, 4.1 scale factors, 4.2 delayed scaling, 4.3 margin);
+ *   [H] the handbook chapter "混合精度与 FP8 训练" (anrans.github.io,
+ *       ai-infra-handbooks), section "FP8 训练": quant / per_tensor /
+ *       per_block, the precision-per-op table, and the hardware notes on
+ *       promoting partial sums every 128 elements.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers (hipMalloc'd or torch CUDA tensors)
+ *     unless stated otherwise.  The caller owns every buffer: the library
+ *     never allocates, frees, synchronizes or copies to the host.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default
+ *     stream.  Every call is asynchronous on that stream.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     return other than FP8Q_OK means nothing was enqueued, except
+ *     FP8Q_EHIP (a launch failed; fp8q_last_error() has the HIP text).
+ *   - Formats: FP8Q_E4M3FN = OCP E4M3FN (bias 7, max 448, no Inf,
+ *     0x7F/0xFF are NaN); FP8Q_E5M2 = OCP E5M2 (bias 15, max 57344) ([A]
+ *     1.2, 1.3).  One code is one byte.
+ *   - Scales are dequantization scales s (x ~= dec(q) * s), fp32:
+ *     s = fl32(fl32(max(amax, eps) * margin) / MAX), MAX = 448 or 57344
+ *     ([H] per_block: amax.clamp(min=1e-12) / MAX; margin from [A] 4.3).
+ *   - Encoding: q = enc(fl32(x / s)) where fl32 is IEEE fp32 division and
+ *     enc rounds to nearest, ties to even, saturates at +-MAX, keeps the
+ *     sign of zero and maps NaN to 0x7F ([H] quant: (x / s).clamp(-MAX,
+ *     MAX).to(FP8)).  Results are bit-identical to that definition.
+ *   - Row-major 2-D operands with leading dimensions in elements.
+ *   - Reentrant; the only global state is the thread-local error text.
+ */
+#ifndef FP8Q_H
+#define FP8Q_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8Q_OK = 0,
+  FP8Q_EINVAL = 1,   /* null pointer, non-positive size, bad enum value  */
+  FP8Q_ESHAPE = 2,   /* a size is not a multiple of 128 where required    */
+  FP8Q_EALIGN = 3,   /* pointer or leading dimension breaks 16-B alignment */
+  FP8Q_EHIP = 4,     /* the HIP runtime refused the launch                */
+  FP8Q_ENOTIMPL = 5  /* combination not provided by this build            */
+} fp8q_status;
+
+typedef enum { FP8Q_F32 = 0, FP8Q_BF16 = 1 } fp8q_dtype;
+typedef enum { FP8Q_E4M3FN = 0, FP8Q_E5M2 = 1 } fp8q_format;
+typedef enum { FP8Q_GRAN_TENSOR = 0, FP8Q_GRAN_1x128 = 1, FP8Q_GRAN_128x128 = 2 } fp8q_gran;
+
+/* Delayed-scaling state ([A] 4.2 DelayedScaler): a window of the last
+ * `window` amax values and the scale derived from them.  Device-resident,
+ * caller-allocated, plain data (copy it to the host to checkpoint it).
+ * `ring` holds the history (first `window` entries used), `pos` the next
+ * slot, `count` the number of values seen (saturating at window), and
+ * `scale` the dequantization scale in force, 1.0 until the window fills. */
+typedef struct {
+  float ring[1024];
+  int32_t window;
+  int32_t count;
+  int32_t pos;
+  float max_val;
+  float eps;
+  float margin;
+  float scale;
+} fp8q_scaler;
+
+/* Library version (major*100 + minor). */
+int fp8q_version(void);
+
+/* Text for a status code; static storage. */
+const char* fp8q_status_string(int status);
+
+/* Text of the last FP8Q_EHIP or validation failure on this thread. */
+const char* fp8q_last_error(void);
+
+/* amax = max_i |x_i| over n elements ([A] 4.1; [H] per_tensor).
+ * x: n elements of dtype dt, 16-B aligned.  amax: one fp32, overwritten
+ * (the call enqueues a 1-thread reset of *amax, then the reduction).
+ * A NaN anywhere gives the quiet NaN 0x7FC00000; +-Inf gives +Inf. */
+int fp8q_amax(const void* x, fp8q_dtype dt, int64_t n, float* amax, void* stream);
+
+/* Per-tensor quantization with a scale held in device memory, the form
+ * delayed scaling uses ([A] 4.2: the scale from earlier steps quantizes
+ * the current tensor; [H] per_tensor).
+ * x: n elements of dtype dt, 16-B aligned.  scale: one fp32 dequant scale
+ * s, read on the device when the kernel runs (e.g. &state->scale).
+ * q: n codes, 16-B aligned.
+ * amax_acc: nullable.  When given, the kernel folds max|x| into it as a
+ *   running maximum: *amax_acc = max(*amax_acc, amax(x)), with NaN
+ *   winning.  It must hold a non-negative value or NaN before the call
+ *   (0 after fp8q_delayed_scaler_update, which consumes and resets it).
+ *   This fuses the amax of delayed scaling into the same pass over x. */
+int fp8q_quantize_tensor(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
+                         uint8_t* q, float* amax_acc, void* stream);
+
+/* Fine-grained 1x128 quantization of activations ([H] per_block(x, 1,
+ * 128); DeepSeek-V3 activation tiling).  For row r and column block kb:
+ *   s = scale(amax(x[r, 128kb : 128kb+128]), eps), q = enc(fl32(x/s)).
+ * x: rows x cols, element (r,c) at x[r*ldx + c]; cols % 128 == 0;
+ *   ldx >= cols; x and ldx*sizeof(dt) 16-B aligned.
+ * q: codes at q[r*ldq + c]; ldq >= cols, 16-B aligned.
+ * scales: fp32 at scales[r*ld_s + kb], ld_s >= cols/128.
+ * eps: lower clamp of amax (the pages use 1e-12); must be > 0. */
+int fp8q_quantize_1x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                        fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
+                        int64_t ld_s, void* stream);
+
+/* Fine-grained 128x128 quantization of weights ([H] per_block(x, 128,
+ * 128)).  As fp8q_quantize_1x128 with one scale per 128x128 tile:
+ * scales[rb*ld_s + kb] for rows 128rb.. and columns 128kb..;
+ * rows % 128 == 0 and cols % 128 == 0. */
+int fp8q_quantize_128x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                          fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
+                          int64_t ld_s, void* stream);
+
+/* Set a device-resident scaler to its initial state ([A] 4.2 __init__):
+ * empty history, scale = 1.0.  window in [1, 1024] (1 gives current
+ * scaling), max_val > 0 (448 or 57344), eps > 0, margin > 0 ([A] 4.3;
+ * 1.0 means none). */
+int fp8q_delayed_scaler_init(fp8q_scaler* state, int32_t window, float max_val, float eps,
+                             float margin, void* stream);
+
+/* One delayed-scaling step ([A] 4.2 update): push *amax into the ring;
+ * once `window` values have been seen, scale = fl32(fl32(max(max(ring),
+ * eps) * margin) / max_val), otherwise the scale stays at its previous
+ * value.  *amax is then reset to 0 so it can accumulate the next step
+ * (see fp8q_quantize_tensor).  A NaN amax propagates into the scale.
+ * Runs as one wavefront; never syncs with the host. */
+int fp8q_delayed_scaler_update(fp8q_scaler* state, float* amax, void* stream);
+
+/* Dequantization x^ = fl32(dec(q) * s) ([H] quant: .float() * scale),
+ * written as fp32 or rounded to nearest-even bf16 (NaN -> quiet NaN).
+ * q: rows x cols codes at q[r*ldq + c].  scales by granularity g:
+ *   TENSOR: scales[0]; 1x128: scales[r*ld_s + c/128];
+ *   128x128: scales[(r/128)*ld_s + c/128].
+ * y: y[r*ldy + c] of dtype out_dt.  cols % 128 == 0 for the block
+ * granularities; q and y 16-B aligned; ldq, ldy multiples of 4 (ignored
+ * when rows == 1, so a flat tensor of any length is rows=1, cols=n). */
+int fp8q_dequantize(const uint8_t* q, fp8q_format f, int64_t rows, int64_t cols, int64_t ldq,
+                    const float* scales, fp8q_gran g, int64_t ld_s, void* y, fp8q_dtype out_dt,
+                    int64_t ldy, void* stream);
+
+/* Block-scaled FP8 GEMM ([A] 3.1 F.linear(x, w) with w stored [out, in];
+ * [H] FP8 inputs with fp32 accumulation, partial sums promoted to fp32
+ * every 128 elements of K):
+ *   C[m,n] = sum_kb (sA[m,kb] * sB(n,kb)) * P_kb[m,n],
+ *   P_kb[m,n] = sum_{k in [128kb, 128kb+128)} dec(A[m,k]) * dec(B[n,k]),
+ * each P_kb formed in fp32 and folded into an fp32 accumulator.
+ * Every product and every in-block sum is carried out in full fp32 (the
+ * codes are decoded exactly and multiplied on the bf16 matrix cores), so
+ * |C - C_exact| stays within a few fp32 roundings of
+ * D[m,n] = sum_kb |sA*sB| * sum_k |dec(a)*dec(b)|.
+ * A: M x K codes of format fa at A[m*lda + k].
+ * sA: 1x128 scales along K at sA[m*sA_sm + kb*sA_skb].
+ * B: N x K codes of format fb at B[n*ldb + k] (the weight as nn.Linear
+ *   stores it, or any K-contiguous operand).
+ * sB: gb = FP8Q_GRAN_128x128: sB[(n/128)*sB_sn + kb*sB_skb] (ceil(N/128) rows);
+ *     gb = FP8Q_GRAN_1x128:   sB[n*sB_sn + kb*sB_skb].
+ * C: M x N at C[m*ldc + n], fp32 or bf16 (round to nearest even).
+ * K % 128 == 0 (else FP8Q_ESHAPE); M, N >= 1 with ragged edges masked;
+ * lda, ldb >= K and multiples of 16; A, B 16-B aligned; ldc >= N.
+ * NaN or Inf codes make the affected outputs non-finite. */
+int fp8q_gemm_blockscaled(const uint8_t* A, fp8q_format fa, int64_t lda, const float* sA,
+                          int64_t sA_sm, int64_t sA_skb, const uint8_t* B, fp8q_format fb,
+                          int64_t ldb, const float* sB, fp8q_gran gb, int64_t sB_sn,
+                          int64_t sB_skb, void* C, fp8q_dtype out_dt, int64_t ldc, int64_t M,
+                          int64_t N, int64_t K, void* stream);
+
+/* The same GEMM with each 128-wide block product P_kb taken from the FP8
+ * matrix cores directly (twice the MFMA rate).  Arguments and layout as
+ * fp8q_gemm_blockscaled.  Inside a block the hardware aligns each group of
+ * eight products to the largest one and drops what lies about 2^-14 below
+ * it -- the limited FP8 accumulator that motivates promotion every 128 K
+ * in [H] -- so the error bound is |C - C_exact| <= 2^-10 * D[m,n] rather
+ * than a few fp32 roundings; the promotion across blocks is fp32. */
+int fp8q_gemm_blockscaled_fast(const uint8_t* A, fp8q_format fa, int64_t lda, const float* sA,
+                               int64_t sA_sm, int64_t sA_skb, const uint8_t* B, fp8q_format fb,
+                               int64_t ldb, const float* sB, fp8q_gran gb, int64_t sB_sn,
+                               int64_t sB_skb, void* C, fp8q_dtype out_dt, int64_t ldc, int64_t M,
+                               int64_t N, int64_t K, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8Q_H */

@@ -41,3 +41,23 @@ def encb():
     L.encb_bits.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
     L.encb_bits.restype = None
     return L
+
+
+@pytest.fixture(scope="session")
+def fq():
+    """The Python binding of libfp8q.so, built with hipcc if nothing is built yet."""
+    import block_scaled_precision_amax_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from block_scaled_precision_amax_amd import build
+        build.build()
+    m.lib()
+    return m
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    """A usable ROCm device; GPU tests fail loudly (not skip) without one."""
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    torch.cuda.init()
+    return torch.device("cuda:0")

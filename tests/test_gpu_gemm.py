@@ -1,0 +1,228 @@
+"""GPU parity of the block-scaled FP8 GEMM against the CPU oracle.
+
+The oracle forms each 128-wide block sum exactly in integers and the outer
+sum in fp64; it also returns D[m,n] = sum_kb |sA*sB| * sum_k |a*b|, the
+scale of any fp32 evaluation's rounding error.  The bar is
+    max_{m,n} |C_gpu - C_ref| / D[m,n] <= 1e-5      (fp32 output)
+i.e. a relative error of 1e-5 measured against the magnitude of the terms
+being summed (a plain |dC|/|C| is unbounded where random signs cancel).
+With bf16 output the kernel's result must equal round-to-nearest-even of
+its own fp32 result, bit for bit.  All calls go through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_amax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = 0, 1
+G1, G128 = 1, 2
+TOL = 1e-5
+
+
+def rand_scales(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.exp(torch.randn(*shape, generator=g) * 2.0 - 4.0).to(torch.float32)
+
+
+def run_gemm(fq, A, fa, sA, B, fb, sB, gb, out=torch.float32, M=None, N=None, K=None, dev="cuda"):
+    M = A.shape[0] if M is None else M
+    N = B.shape[0] if N is None else N
+    K = A.shape[1] if K is None else K
+    C = torch.full((M, N), float("nan"), dtype=out, device=dev)
+    Ad, Bd, sAd, sBd = A.to(dev), B.to(dev), sA.to(dev), sB.to(dev)
+    fq.fp8q_gemm_blockscaled(Ad, fa, A.shape[1], sAd, sA.shape[1], 1, Bd, fb, B.shape[1], sBd, gb, sB.shape[1],
+                             1, C, N, M, N, K)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+def check(Cg, Cref, D, what=""):
+    Cg = Cg.to(torch.float64).numpy()
+    err = np.abs(Cg - Cref)
+    assert np.all(np.isfinite(Cg)), what
+    ratio = np.where(D > 0, err / np.where(D > 0, D, 1), np.where(err > 0, np.inf, 0))
+    worst = float(ratio.max())
+    assert worst <= TOL, f"{what}: max |dC|/D = {worst:.3e}"
+    return worst
+
+
+def bf16_of(c32):
+    return c32.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fa,fb,gb", [(E4, E4, G128), (E5, E4, G128), (E5, E4, G1), (E4, E5, G128),
+                                      (E5, E5, G1), (E4, E4, G1)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (64, 128, 128), (1, 256, 256), (300, 200, 384)])
+def test_gemm_random_codes(fq, orc, gpu, fa, fb, gb, M, N, K):
+    """Uniformly random finite codes (the whole code space), random scales,
+    ragged M and N, several K blocks."""
+    A = W.fp8_codes((M, K), fa, seed=M + K)
+    B = W.fp8_codes((N, K), fb, seed=N + K + 1)
+    sA = rand_scales((M, K // 128), 1)
+    sB = rand_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 2)
+    C32 = run_gemm(fq, A, fa, sA, B, fb, sB, gb)
+    Cref, D = orc.gemm_blockscaled(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb)
+    check(C32, Cref, D, f"{M}x{N}x{K}")
+    Cb = run_gemm(fq, A, fa, sA, B, fb, sB, gb, out=torch.bfloat16)
+    assert torch.equal(Cb.view(torch.int16), bf16_of(C32).view(torch.int16))
+
+
+def test_gemm_strided_operands(fq, orc, gpu):
+    """lda, ldb > K and scale strides other than the packed ones."""
+    M, N, K, ld = 130, 256, 256, 384
+    A = W.fp8_codes((M, ld), E4, seed=5)
+    B = W.fp8_codes((N, ld), E4, seed=6)
+    sA_full = rand_scales((K // 128, M), 7)          # transposed storage: sA[m*1 + kb*M]
+    sB = rand_scales((N // 128, K // 128), 8)
+    C = torch.empty(M, N + 8, dtype=torch.float32, device=gpu)
+    fq.fp8q_gemm_blockscaled(A.to(gpu), E4, ld, sA_full.to(gpu), 1, M, B.to(gpu), E4, ld, sB.to(gpu), G128,
+                             K // 128, 1, C, N + 8, M, N, K)
+    torch.cuda.synchronize()
+    sA = sA_full.t().contiguous()
+    Cref, D = orc.gemm_blockscaled(A[:, :K].numpy(), E4, sA.numpy(), B[:, :K].numpy(), E4, sB.numpy(), G128)
+    check(C.cpu()[:, :N], Cref, D)
+
+
+def test_gemm_special_codes_non_finite(fq, orc, gpu):
+    M, N, K = 64, 128, 256
+    A = W.fp8_codes((M, K), E4, seed=9)
+    B = W.fp8_codes((N, K), E4, seed=10)
+    A[3, 17] = 0x7F  # NaN
+    B[5, 200] = 0xFF
+    sA = rand_scales((M, 2), 11)
+    sB = rand_scales((1, 2), 12)
+    C = run_gemm(fq, A, E4, sA, B, E4, sB, G128)
+    Cref, _ = orc.gemm_blockscaled(A.numpy(), E4, sA.numpy(), B.numpy(), E4, sB.numpy(), G128)
+    assert np.array_equal(~np.isfinite(C.numpy()), np.isnan(Cref))
+
+
+def test_gemm_zero_and_identity(fq, orc, gpu):
+    """All-zero A gives exact zeros; B = identity codes returns dec(A)*sA*sB exactly."""
+    M, K = 96, 256
+    A = W.fp8_codes((M, K), E4, seed=13)
+    B = torch.zeros(K, K, dtype=torch.uint8)
+    B[torch.arange(K), torch.arange(K)] = 0x38  # 1.0
+    sA = rand_scales((M, 2), 14)
+    sB = torch.ones(2, 2)
+    C = run_gemm(fq, A, E4, sA, B, E4, sB, G128)
+    Cref, D = orc.gemm_blockscaled(A.numpy(), E4, sA.numpy(), B.numpy(), E4, sB.numpy(), G128)
+    assert np.array_equal(C.numpy().astype(np.float64), Cref)
+    Z = run_gemm(fq, torch.zeros_like(A), E4, sA, B, E4, sB, G128)
+    assert torch.count_nonzero(Z) == 0
+
+
+def quantized_operands(orc, a32, fa, b32, fb, gb):
+    """Quantize fp32 operands with the oracle (codes and scales are the
+    inputs of the GEMM; the GEMM parity does not depend on who made them)."""
+    qa, sa = orc.quantize_blocks(a32, 1, 128, fa)
+    if gb == G128:
+        qb, sb = orc.quantize_blocks(b32, 128, 128, fb)
+    else:
+        qb, sb = orc.quantize_blocks(b32, 1, 128, fb)
+    return torch.from_numpy(qa), torch.from_numpy(sa), torch.from_numpy(qb), torch.from_numpy(sb)
+
+
+def sampled_rows(M, n=64):
+    """One row per band of M/n rows, deterministic, first and last included."""
+    r = np.unique(np.concatenate([np.linspace(0, M - 1, n).astype(np.int64), [0, M - 1]]))
+    return r
+
+
+def test_gemm_4096_cubed_sampled(fq, orc, gpu):
+    """M = N = K = 4096, A from N(0,1) with 4 outlier columns x100 (1x128),
+    B 0.02*N(0,1) (128x128), E4M3FN; fp32 output compared on 64 sampled rows,
+    bf16 output checked against the fp32 result everywhere."""
+    a = W.activation(4096, 4096, seed=3, factor=100.0).numpy()
+    b = W.weight(4096, 4096, seed=30).numpy()
+    qa, sa, qb, sb = quantized_operands(orc, a, E4, b, E4, G128)
+    C32 = run_gemm(fq, qa, E4, sa, qb, E4, sb, G128)
+    rows = sampled_rows(4096)
+    Cref, D = orc.gemm_blockscaled(qa.numpy(), E4, sa.numpy(), qb.numpy(), E4, sb.numpy(), G128, rows=rows)
+    check(C32[rows], Cref, D, "4096^3")
+    Cb = run_gemm(fq, qa, E4, sa, qb, E4, sb, G128, out=torch.bfloat16)
+    assert torch.equal(Cb.view(torch.int16), bf16_of(C32).view(torch.int16))
+
+
+def test_gemm_llm_layer_sampled(fq, orc, gpu):
+    """M=16384, N=18432, K=7168 (activation bf16 with 4 outlier columns x1e3
+    quantized 1x128, weight 0.02*N(0,1) 128x128), 16 sampled rows."""
+    M, N, K = 16384, 18432, 7168
+    x = W.activation(M, K, seed=4, factor=1e3, dtype=torch.bfloat16, device=gpu)
+    w = W.weight(N, K, seed=40, device=gpu)
+    qa = torch.empty(M, K, dtype=torch.uint8, device=gpu)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=gpu)
+    qb = torch.empty(N, K, dtype=torch.uint8, device=gpu)
+    sb = torch.empty(N // 128, K // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_1x128(x, M, K, K, E4, 1e-12, qa, K, sa, K // 128)
+    fq.fp8q_quantize_128x128(w, N, K, K, E4, 1e-12, qb, K, sb, K // 128)
+    C = torch.empty(M, N, dtype=torch.float32, device=gpu)
+    fq.fp8q_gemm_blockscaled(qa, E4, K, sa, K // 128, 1, qb, E4, K, sb, G128, K // 128, 1, C, N, M, N, K)
+    torch.cuda.synchronize()
+    rows = sampled_rows(M, 16)
+    Cref, D = orc.gemm_blockscaled(qa[rows].cpu().numpy(), E4, sa[rows].cpu().numpy(), qb.cpu().numpy(), E4,
+                                   sb.cpu().numpy(), G128)
+    check(C[rows].cpu(), Cref, D, "llm layer")
+
+
+@pytest.mark.parametrize("kind", ["dgrad", "wgrad"])
+def test_gemm_backward_shapes_sampled(fq, orc, gpu, kind):
+    """dgrad: 16384x4096x4096 with E5M2 gradients (1x128) times an E4M3FN
+    128x128 weight; wgrad: 4096x4096 over K=16384 tokens with 1x128 scales
+    on both operands.  fp32 output, 16 sampled rows."""
+    if kind == "dgrad":
+        M, N, K = 16384, 4096, 4096
+        a = W.gradient(M, K, seed=5).numpy()
+        b = W.weight(N, K, seed=50).numpy()
+        gb = G128
+    else:
+        M, N, K = 4096, 4096, 16384
+        a = W.gradient(M, K, seed=51).numpy()
+        b = W.normal((N, K), seed=52).numpy()
+        gb = G1
+    qa, sa, qb, sb = quantized_operands(orc, a, E5, b, E4, gb)
+    C = run_gemm(fq, qa, E5, sa, qb, E4, sb, gb)
+    rows = sampled_rows(M, 16)
+    Cref, D = orc.gemm_blockscaled(qa.numpy(), E5, sa.numpy(), qb.numpy(), E4, sb.numpy(), gb, rows=rows)
+    check(C[rows], Cref, D, kind)
+
+
+# ------------------------------------------------------------------ the FP8-MFMA path
+FAST_TOL = 2.0 ** -10  # the header's bound for in-block FP8 accumulation
+
+
+def run_gemm_fast(fq, A, fa, sA, B, fb, sB, gb, out=torch.float32, dev="cuda"):
+    M, K = A.shape
+    N = B.shape[0]
+    C = torch.full((M, N), float("nan"), dtype=out, device=dev)
+    fq.fp8q_gemm_blockscaled_fast(A.to(dev), fa, K, sA.to(dev), sA.shape[1], 1, B.to(dev), fb, K, sB.to(dev), gb,
+                                  sB.shape[1], 1, C, N, M, N, K)
+    torch.cuda.synchronize()
+    return C.cpu()
+
+
+@pytest.mark.parametrize("fa,fb,gb", [(E4, E4, G128), (E5, E4, G128), (E5, E4, G1), (E4, E5, G1)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (300, 200, 384)])
+def test_gemm_fast_random_codes(fq, orc, gpu, fa, fb, gb, M, N, K):
+    A = W.fp8_codes((M, K), fa, seed=M + K)
+    B = W.fp8_codes((N, K), fb, seed=N + K + 1)
+    sA = rand_scales((M, K // 128), 1)
+    sB = rand_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 2)
+    C = run_gemm_fast(fq, A, fa, sA, B, fb, sB, gb).to(torch.float64).numpy()
+    Cref, D = orc.gemm_blockscaled(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb)
+    assert np.all(np.abs(C - Cref) <= FAST_TOL * D)
+    Cb = run_gemm_fast(fq, A, fa, sA, B, fb, sB, gb, out=torch.bfloat16)
+    assert torch.equal(Cb.view(torch.int16), torch.from_numpy(C).float().to(torch.bfloat16).view(torch.int16))
+
+
+def test_gemm_fast_4096_cubed_sampled(fq, orc, gpu):
+    a = W.activation(4096, 4096, seed=3, factor=100.0).numpy()
+    b = W.weight(4096, 4096, seed=30).numpy()
+    qa, sa, qb, sb = quantized_operands(orc, a, E4, b, E4, G128)
+    C = run_gemm_fast(fq, qa, E4, sa, qb, E4, sb, G128)
+    rows = sampled_rows(4096)
+    Cref, D = orc.gemm_blockscaled(qa.numpy(), E4, sa.numpy(), qb.numpy(), E4, sb.numpy(), G128, rows=rows)
+    err = np.abs(C[rows].to(torch.float64).numpy() - Cref)
+    assert np.all(err <= FAST_TOL * D)
