@@ -13,20 +13,21 @@
 // group of eight K positions to the group's largest one and drop what lies
 // about 2^-14 below it.  Two paths share one tiled kernel:
 //   * exact (fp8q_gemm_blockscaled): the codes are decoded to bf16 (lossless
-//     for E4M3 and E5M2) and multiplied by v_mfma_f32_32x32x16_bf16, whose
+//     for E4M3 and E5M2) and multiplied by v_mfma_f32_16x16x32_bf16, whose
 //     products and sums are exact fp32, so P_kb is the fp32 sum the method
 //     asks for;
-//   * fast (fp8q_gemm_blockscaled_fast): v_mfma_f32_32x32x64_f8f6f4 on the
-//     codes themselves, twice the MFMA rate, with the hardware's own
-//     accumulation inside each 128 block (the situation the handbook's
-//     promotion rule is written for).
+//   * fast (fp8q_gemm_blockscaled_fast): v_mfma_f32_16x16x128_f8f6f4 on the
+//     codes themselves -- one instruction per 16x16 tile and K block, twice
+//     the MFMA rate -- with the hardware's own accumulation inside each
+//     128 block (the situation the handbook's promotion rule is written for).
 //
-// Tiling: a 128x128 output tile per workgroup of four wavefronts (2x2, each
-// 64x64 = 2x2 MFMA tiles of 32x32).  Per 128-wide K block the A and B code
-// tiles (16 KB each) are staged into LDS, double buffered, from registers
-// loaded one block ahead; rows are XOR-swizzled in 16-byte chunks so the
-// fragment reads hit distinct banks.  The 1x128 A scales of the tile's 128
-// rows travel with the codes.  Workgroups are renumbered so that each of
+// Tiling: a 256x256 output tile per workgroup of eight wavefronts (2x4,
+// each 128x64 = 8x4 MFMA tiles of 16x16).  Per 128-wide K block the A and B
+// code tiles (32 KB each) are copied into LDS by the global-to-LDS load
+// path, double buffered and one block ahead, with an XOR chunk swizzle that
+// keeps the fragment reads free of bank conflicts.  The per-row promotion
+// coefficient sA*sB of the tile's 256 rows travels with the codes, so
+// promotion is one FMA per output element and K block.  Workgroups are renumbered so that each of
 // the eight XCDs (one L2 each) walks a contiguous, M-grouped part of the
 // tile grid.
 #include "fp8q_internal.h"
@@ -35,20 +36,26 @@ namespace fp8q {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-static constexpr int BM = 128, BN = 128, BK = 128;
-static constexpr int kGemmThreads = 256;
+static constexpr int BK = 128;
+static constexpr int kGemmThreads = 512;  // eight wavefronts, 2 x 4
 
-// Byte offset of (row, k) in a swizzled 128-row x 128-byte code tile: the
-// 16-byte chunk index is XORed with row%8 and the 8-byte half with
-// (row/8)%2, so 16 consecutive rows read at one k cover all 32 banks.
-__device__ __forceinline__ int swz(int row, int k) {
-  return row * BK + ((((k >> 4) ^ row) & 7) << 4) + ((k & 15) ^ (((row >> 3) & 1) << 3));
-}
+// Per path: wavefront grid (2 x 4) and MFMA tiles of 16x16 per wavefront.
+// FP8 path: 8 x 4 tiles (128 x 64 per wavefront, 256 x 256 per workgroup);
+// exact path: 4 x 4 tiles (64 x 64, 128 x 256), which leaves room for the
+// decoded bf16 fragments in the 256 registers a lane has at two
+// wavefronts per SIMD.
+template <bool FAST>
+struct Cfg {
+  static constexpr int WGM = 2, WGN = 4;
+  static constexpr int TI = FAST ? 8 : 4, TJ = 4;
+  static constexpr int BM = WGM * TI * 16, BN = WGN * TJ * 16;
+};
 
 // Two FP8 codes (bytes 0-1 or 2-3 of w) -> two bf16, exact.
 template <int FMT, bool HI>
@@ -69,6 +76,12 @@ __device__ __forceinline__ v8bf dec8_bf16(u32x2 w) {
   return r;
 }
 
+// An empty asm that claims to read and rewrite v: the value must exist in
+// registers at this point of the program, which keeps the compiler from
+// sinking or batching the pure MFMA / FMA arithmetic around it and so keeps
+// the software pipeline below in the order it is written.
+__device__ __forceinline__ void pin(v4f& v) { asm volatile("" : "+v"(v)); }
+
 // Workgroup id -> (tile row, tile column).  Consecutive ids go to the
 // eight XCDs in turn; renumber so each XCD gets a contiguous range, then
 // walk that range in groups of 8 tile rows (column-major inside a group)
@@ -87,170 +100,277 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nbid, int64_t ntm, 
   tn = r / gs;
 }
 
+// LDS layout of a staged R-row x 128-byte code tile: rows are stored
+// unpadded, and the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7)
+// of that row.  Sixteen consecutive rows read at one K offset with 16-byte
+// reads then cover every bank once per 256 bytes (measured on gfx950: the
+// full ~128 B/clk of ds_read_b128, against half of it without the XOR).
+// Every fragment row of a lane has the same r % 16, so the XOR term is a
+// per-lane constant.
+__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+// Byte offsets (from the operand's base) of the 16-byte chunks a lane copies
+// into LDS for one R-row code tile: the tile is R/8 loads of 1 KB, R/64 per
+// wavefront; lane l of load g fills LDS bytes 16*(64g + l) .. +16, i.e. slot
+// (64g+l)%8 of row (64g+l)/8, with the global chunk that belongs there.
+// Rows past the matrix edge read its last row instead (their results are
+// never stored).  The host keeps every operand under 4 GiB so the offsets
+// fit 32 bits.
+template <int R>
+__device__ __forceinline__ void dma_offsets(uint32_t* off, int64_t ld, int64_t r0, int64_t rows, int wave,
+                                            int lane) {
+#pragma unroll
+  for (int u = 0; u < R / 64; ++u) {
+    const int slot = (wave * (R / 64) + u) * 64 + lane, r = slot >> 3, pc = slot & 7;
+    int64_t gr = r0 + r;
+    gr = gr < rows ? gr : rows - 1;
+    off[u] = (uint32_t)(gr * ld + 16 * swz_chunk(r, pc));
+  }
+}
+
+// Issues the loads of one tile: base is the operand advanced to the K block.
+template <int R>
+__device__ __forceinline__ void dma_tile(uint8_t* lds, const uint8_t* base, const uint32_t* off, int wave) {
+#pragma unroll
+  for (int u = 0; u < R / 64; ++u)
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + off[u]),
+                                     (__attribute__((address_space(3))) void*)(lds + (wave * (R / 64) + u) * 1024),
+                                     16, 0, 0);
+}
+
+// One workgroup of eight wavefronts computes a BM x BN tile of C; wavefront
+// (wm, wn) = (w/4, w%4) owns TI x TJ MFMA tiles of 16x16 at rows
+// 16*TI*wm.. and columns 16*TJ*wn.. (64 columns: inside one 128-column
+// block of B scales).  Each tile's block product P_kb comes from the 16x16
+// MFMA(s) of that block and is folded into the tile's accumulator while
+// the next row tile's MFMAs run: the loop is software-pipelined by hand
+// and fenced step by step, so at most two row tiles of P are live and the
+// promotion FMAs (and, on the exact path, the decodes of the next
+// fragments) sit in the MFMA shadow.
 template <int FA, int FB, int GB, int ODT, bool FAST>
-__global__ __launch_bounds__(kGemmThreads, 2) void k_gemm(
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t sA_sm,
     int64_t sA_skb, const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
     int64_t sB_sn, int64_t sB_skb, void* __restrict__ C, int64_t ldc, int64_t M, int64_t N,
     int64_t K, int64_t ntm, int64_t ntn) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_b[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) float lds_sa[2][BM];
+  using G = Cfg<FAST>;
+  constexpr int BM = G::BM, BN = G::BN, TI = G::TI, TJ = G::TJ;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2][BN * BK];
+  __shared__ __attribute__((aligned(16))) float lds_sa[2][BM];  // 1x128 A scales of the tile's rows
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
   int64_t tm, tn;
   tile_of(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t nkb = K / BK;
 
-  // ---- global -> register staging: 1024 16-byte chunks per operand tile,
-  // four per thread: chunk c = tid + 256*j is row c/8, bytes 16*(c%8).
-  u32x4 ra[4], rb[4];
+  const float* sa_row = sA + ((m0 + tid < M) ? m0 + tid : M - 1) * sA_sm;
   float rsa = 0.0f;
-  auto load_tiles = [&](int64_t kb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + kGemmThreads * j, row = c >> 3, ch = c & 7;
-      const int64_t gm = m0 + row, gn = n0 + row;
-      ra[j] = gm < M ? *(const u32x4*)(A + gm * lda + kb * BK + ch * 16) : u32x4{0u, 0u, 0u, 0u};
-      rb[j] = gn < N ? *(const u32x4*)(B + gn * ldb + kb * BK + ch * 16) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < BM) {
-      const int64_t gm = (m0 + tid < M) ? m0 + tid : M - 1;
-      rsa = sA[gm * sA_sm + kb * sA_skb];
-    }
-  };
-  auto store_tiles = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + kGemmThreads * j, row = c >> 3, ch = c & 7;
-      // the 8-byte halves trade places on odd row octets (see swz)
-      const bool sw = (row >> 3) & 1;
-      const int off = row * BK + (((ch ^ row) & 7) << 4);
-      u32x4 va = ra[j], vb = rb[j];
-      if (sw) {
-        va = u32x4{va.z, va.w, va.x, va.y};
-        vb = u32x4{vb.z, vb.w, vb.x, vb.y};
-      }
-      *(u32x4*)(&lds_a[s][off]) = va;
-      *(u32x4*)(&lds_b[s][off]) = vb;
-    }
-    if (tid < BM) lds_sa[s][tid] = rsa;
-  };
+  uint32_t a_off[BM / 64], b_off[BN / 64];
+  dma_offsets<BM>(a_off, lda, m0, M, wave, lane);
+  dma_offsets<BN>(b_off, ldb, n0, N, wave, lane);
 
-  v16f acc[2][2];
+  v4f acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = v16f{};
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // rows/columns this lane owns in the 32x32 results: column l%32, rows
-  // 8*(e/4) + 4*(l/32) + e%4 for e = 0..15
-  const int lr = lane & 31, lh = lane >> 5;
+  // 16x16 results: column l%16, rows 4*(l/16) + e.  Operand fragments: row
+  // (A) / column (B) l%16 and K bytes chosen by l/16 (the same K for A and B).
+  const int lr = lane & 15, lq = lane >> 4;
+  const int a_row0 = (wm * TI * 16 + lr) * BK, b_row0 = (wn * TJ * 16 + lr) * BK;
+  const int64_t wcol0 = n0 + wn * TJ * 16;  // first column of this wavefront
+  uint32_t col_s[TJ];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t col = wcol0 + 16 * j + lr;
+    col_s[j] = (uint32_t)((col < N ? col : N - 1) * sB_sn);
+  }
+  const float* sb_blk = sB + (wcol0 >> 7) * sB_sn;
 
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
-  for (int64_t kb = 0; kb < nkb; ++kb) {
+  // P_kb of every MFMA tile of the wavefront, folded into acc
+  auto compute = [&](int64_t kb) {
     const int s = (int)(kb & 1);
-    if (kb + 1 < nkb) load_tiles(kb + 1);
-
-    // ---- P_kb for the wave's 2x2 tiles of 32x32
-    v16f p[2][2];
+    // the B scale(s) of this wavefront's columns
+    float sbv[TJ];
+    float sbw = 1.0f;
+    if constexpr (GB == FP8Q_GRAN_128x128) {
+      sbw = sb_blk[kb * sB_skb];
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) p[i][j] = v16f{};
-    const uint8_t* la = lds_a[s];
-    const uint8_t* lb = lds_b[s];
+      for (int j = 0; j < TJ; ++j) sbv[j] = (sB + kb * sB_skb)[col_s[j]];
+    }
+    const uint8_t* la = lds_a[s] + a_row0;
+    const uint8_t* lb = lds_b[s] + b_row0;
+    const float* lc = lds_sa[s] + wm * TI * 16 + 4 * lq;
+    auto coef = [&](int i) {
+      const float4 c4 = *(const float4*)(lc + 16 * i);
+      v4f c = {c4.x, c4.y, c4.z, c4.w};
+      if constexpr (GB == FP8Q_GRAN_128x128) c = c * sbw;
+      return c;
+    };
+    // one promotion FMA: acc[i][j][e] += P * (sA * sB)
+    auto fold = [&](int i, int j, int e, float p, const v4f& c) {
+      if constexpr (GB == FP8Q_GRAN_128x128)
+        acc[i][j][e] = __builtin_fmaf(p, c[e], acc[i][j][e]);
+      else
+        acc[i][j][e] = __builtin_fmaf(p * c[e], sbv[j], acc[i][j][e]);
+    };
+    v4f pp[TJ], pn[TJ];
+    v4f cp = {0.0f, 0.0f, 0.0f, 0.0f}, cc = coef(0);
     if constexpr (FAST) {
-      // 32x32x64: lane holds 32 bytes of K (32*(l/32) .. +32) of one row
+      // 16x16x128: the lane holds logical chunks 2q, 2q+1 (q = l/16) of its row
+      const int o0 = 16 * swz_chunk(lr, 2 * lq), o1 = 16 * swz_chunk(lr, 2 * lq + 1);
+      auto frag = [&](const uint8_t* base) {
+        const u32x4 x0 = *(const u32x4*)(base + o0);
+        const u32x4 x1 = *(const u32x4*)(base + o1);
+        return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      };
+      v8i fb[TJ];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        v8i fa[2], fb[2];
+      for (int j = 0; j < TJ; ++j) fb[j] = frag(lb + 16 * j * BK);
+      v8i fa = frag(la), fn = fa;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int ra_ = wm * 64 + 32 * i + lr, rb_ = wn * 64 + 32 * i + lr;
-          const int k = 64 * kk + 32 * lh;
-          const u32x4 a0 = *(const u32x4*)(la + swz(ra_, k) - (((ra_ >> 3) & 1) << 3));
-          const u32x4 a1 = *(const u32x4*)(la + swz(ra_, k + 16) - (((ra_ >> 3) & 1) << 3));
-          const u32x4 b0 = *(const u32x4*)(lb + swz(rb_, k) - (((rb_ >> 3) & 1) << 3));
-          const u32x4 b1 = *(const u32x4*)(lb + swz(rb_, k + 16) - (((rb_ >> 3) & 1) << 3));
-          const bool swa = (ra_ >> 3) & 1, swb = (rb_ >> 3) & 1;
-          const u32x4 A0 = swa ? u32x4{a0.z, a0.w, a0.x, a0.y} : a0;
-          const u32x4 A1 = swa ? u32x4{a1.z, a1.w, a1.x, a1.y} : a1;
-          const u32x4 B0 = swb ? u32x4{b0.z, b0.w, b0.x, b0.y} : b0;
-          const u32x4 B1 = swb ? u32x4{b1.z, b1.w, b1.x, b1.y} : b1;
-          fa[i] = v8i{(int)A0.x, (int)A0.y, (int)A0.z, (int)A0.w, (int)A1.x, (int)A1.y, (int)A1.z, (int)A1.w};
-          fb[i] = v8i{(int)B0.x, (int)B0.y, (int)B0.z, (int)B0.w, (int)B1.x, (int)B1.y, (int)B1.z, (int)B1.w};
+      for (int i = 0; i < TI; ++i) {
+        v4f cn = cc;
+        if (i + 1 < TI) {
+          fn = frag(la + 16 * (i + 1) * BK);
+          cn = coef(i + 1);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < TJ; ++j) {
+          pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, FA,
+                                                                  FB, 0, 0, 0, 0);
+          pin(pn[j]);
+          if (i > 0) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            p[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[i], fb[j], p[i][j], FA, FB, 0, 0, 0, 0);
+            for (int e = 0; e < 4; ++e) fold(i - 1, j, e, pp[j][e], cp);
+            pin(acc[i - 1][j]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
+        cp = cc;
+        cc = cn;
+        fa = fn;
       }
     } else {
-      // 32x32x16 bf16: lane holds 8 codes of K (16*kk + 8*(l/32) .. +8) of one row
+      // 16x16x32 bf16, four per block.  Inside the block the K positions are
+      // assigned so that lane group q (= l/16) owns the contiguous bytes
+      // 32q .. 32q+32 of the block for all four MFMAs, bytes 8kk .. +8 of
+      // them going to MFMA kk; A and B use the same assignment, so every
+      // product still pairs matching k.  Each lane reads its 32 bytes with
+      // two 16-byte LDS reads, as on the FP8 path.
+      const int o0 = 16 * swz_chunk(lr, 2 * lq), o1 = 16 * swz_chunk(lr, 2 * lq + 1);
+      auto raw32 = [&](const uint8_t* base, u32x2* r) {
+        const u32x4 x0 = *(const u32x4*)(base + o0);
+        const u32x4 x1 = *(const u32x4*)(base + o1);
+        r[0] = u32x2{x0.x, x0.y};
+        r[1] = u32x2{x0.z, x0.w};
+        r[2] = u32x2{x1.x, x1.y};
+        r[3] = u32x2{x1.z, x1.w};
+      };
+      v8bf fb[TJ][4];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        v8bf fa[2], fb[2];
+      for (int j = 0; j < TJ; ++j) {
+        u32x2 r[4];
+        raw32(lb + 16 * j * BK, r);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int ra_ = wm * 64 + 32 * i + lr, rb_ = wn * 64 + 32 * i + lr;
-          const int k = 16 * kk + 8 * lh;
-          fa[i] = dec8_bf16<FA>(*(const u32x2*)(la + swz(ra_, k)));
-          fb[i] = dec8_bf16<FB>(*(const u32x2*)(lb + swz(rb_, k)));
+        for (int kk = 0; kk < 4; ++kk) fb[j][kk] = dec8_bf16<FB>(r[kk]);
+      }
+      v8bf fa[4];
+      {
+        u32x2 r[4];
+        raw32(la, r);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) fa[kk] = dec8_bf16<FA>(r[kk]);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        u32x2 raw[4];
+        v4f cn = cc;
+        if (i + 1 < TI) {
+          raw32(la + 16 * (i + 1) * BK, raw);
+          cn = coef(i + 1);
+        }
+        v2bf part[4][4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) {
+            pn[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk], fb[j][kk],
+                                                            kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j], 0, 0, 0);
+            pin(pn[j]);
+            if (i > 0) {
+              fold(i - 1, j, kk, pp[j][kk], cp);
+              pin(acc[i - 1][j]);
+            }
+            if (i + 1 < TI) {
+              // decode part j (two codes) of the next row tile's fragment kk
+              const uint32_t w = (j & 2) ? raw[kk].y : raw[kk].x;
+              part[kk][j] = (j & 1) ? dec2_bf16<FA, true>(w) : dec2_bf16<FA, false>(w);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        if (i + 1 < TI) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            v8bf f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              f[2 * q] = part[kk][q][0];
+              f[2 * q + 1] = part[kk][q][1];
+            }
+            fa[kk] = f;
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            p[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], p[i][j], 0, 0, 0);
+        for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
+        cp = cc;
+        cc = cn;
       }
     }
+    // the last row tile's promotion
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fold(TI - 1, j, e, pp[j][e], cp);
+  };
 
-    // ---- promotion: acc += P_kb * (sA[m,kb] * sB(n,kb))
-    float sbv[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int64_t col = n0 + wn * 64 + 32 * j + lr;
-      col = col < N ? col : N - 1;
-      sbv[j] = GB == FP8Q_GRAN_128x128 ? sB[(col >> 7) * sB_sn + kb * sB_skb] : sB[col * sB_sn + kb * sB_skb];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const float* sap = lds_sa[s] + wm * 64 + 32 * i + 4 * lh;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 sa4 = *(const float4*)(sap + 8 * q);
-        const float sa[4] = {sa4.x, sa4.y, sa4.z, sa4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j][4 * q + e] = __builtin_fmaf(p[i][j][4 * q + e], sa[e] * sbv[j], acc[i][j][4 * q + e]);
-      }
-    }
+  dma_tile<BM>(lds_a[0], A, a_off, wave);
+  dma_tile<BN>(lds_b[0], B, b_off, wave);
+  if (tid < BM) lds_sa[0][tid] = sa_row[0];
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-    if (kb + 1 < nkb) {
-      store_tiles(s ^ 1);
-    }
+  // steady state: copy block kb+1 while computing block kb, no branches
+  for (int64_t kb = 0; kb + 1 < nkb; ++kb) {
+    const int s = (int)(kb & 1);
+    dma_tile<BM>(lds_a[s ^ 1], A + (kb + 1) * BK, a_off, wave);
+    dma_tile<BN>(lds_b[s ^ 1], B + (kb + 1) * BK, b_off, wave);
+    if (tid < BM) rsa = sa_row[(kb + 1) * sA_skb];
+    compute(kb);
+    if (tid < BM) lds_sa[s ^ 1][tid] = rsa;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
+  compute(nkb - 1);
 
   // ---- epilogue
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t col = n0 + wn * 64 + 32 * j + lr;
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t col = wcol0 + 16 * j + lr;
     if (col >= N) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * lh + (e & 3);
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * TI * 16 + 16 * i + 4 * lq + e;
         if (row >= M) continue;
         if constexpr (ODT == FP8Q_F32)
           __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
@@ -264,6 +384,7 @@ template <int FA, int FB, int GB, int ODT, bool FAST>
 static void launch_t(const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
                      const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn, int64_t sB_skb, void* C,
                      int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  constexpr int BM = Cfg<FAST>::BM, BN = Cfg<FAST>::BN;
   const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   hipLaunchKernelGGL((k_gemm<FA, FB, GB, ODT, FAST>), dim3((unsigned)(ntm * ntn)), dim3(kGemmThreads), 0, st, A,
                      lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, M, N, K, ntm, ntn);
@@ -310,8 +431,12 @@ int launch_gemm(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t 
                 int64_t sA_skb, const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb,
                 int64_t sB_sn, int64_t sB_skb, void* C, int out_dt, int64_t ldc, int64_t M,
                 int64_t N, int64_t K, bool fast, hipStream_t st) {
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
   if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "gemm: more than 2^31-1 output tiles");
+  // per-lane operand offsets are 32-bit
+  if ((M - 1) * lda + K > 0xFFFFFFFFll || (N - 1) * ldb + K > 0xFFFFFFFFll ||
+      (gb == FP8Q_GRAN_1x128 && (N - 1) * sB_sn > 0x3FFFFFFFll))
+    return fail(FP8Q_ESHAPE, "gemm: an operand spans 4 GiB or more");
   if (fast)
     dispatch_f<true>(fa, fb, gb, out_dt, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, M, N, K, st);
   else
