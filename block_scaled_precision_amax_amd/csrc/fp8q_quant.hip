@@ -34,6 +34,14 @@ __device__ __forceinline__ uint32_t pk_fold(uint32_t acc) {
   return max(acc & 0xFFFFu, acc >> 16) << 16;
 }
 
+// Folds a workgroup's maximum into *p.  The accumulator only grows, so a
+// workgroup whose maximum does not exceed the value already there skips the
+// atomic: one relaxed read instead of an atomic per workgroup, which
+// otherwise serialize on the one address.
+__device__ __forceinline__ void fold_max(uint32_t* p, uint32_t m) {
+  if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
+}
+
 // Workgroup-wide maximum of one value per thread (kThreads threads).
 __device__ __forceinline__ uint32_t block_max(uint32_t v) {
   __shared__ uint32_t part[kThreads / 64];
@@ -53,43 +61,66 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 // One read of x; per-thread max of |x| bit patterns, then one atomic max
 // per workgroup on the fp32 pattern (non-negative floats order like their
 // bit patterns, so the result does not depend on the order).
+// Work is cut into contiguous chunks of kU x 256 16-byte vectors;
+// each workgroup walks its own chunks, lanes on consecutive addresses in
+// every load.  On gfx950 this keeps HBM streaming near its best rate at any
+// grid size, where grid-strided vectors lose up to a quarter of it.
+// Per-kernel chunk depth (16-byte vectors per lane) and persistent grid
+// (workgroups per CU), chosen by measurement on MI355X: the read-only amax
+// wants few long-lived workgroups, the quantizers more wavefronts in flight
+// to cover their arithmetic.
+#ifndef FP8Q_KU_A
+#define FP8Q_KU_A 8
+#endif
+#ifndef FP8Q_G_A
+#define FP8Q_G_A 2
+#endif
+#ifndef FP8Q_KU_T
+#define FP8Q_KU_T 2
+#endif
+#ifndef FP8Q_G_T
+#define FP8Q_G_T 16
+#endif
+#ifndef FP8Q_G_1
+#define FP8Q_G_1 12
+#endif
+#ifndef FP8Q_KU_D
+#define FP8Q_KU_D 4
+#endif
+#ifndef FP8Q_G_D
+#define FP8Q_G_D 8
+#endif
+
+template <int DT>
+__device__ __forceinline__ uint32_t vec_absmax(uint32_t m, const u32x4& v) {
+  if constexpr (DT == FP8Q_F32) {
+    m = max(m, max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu));
+    return max(m, max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
+  } else {
+    m = pk_absmax(m, v.x);
+    m = pk_absmax(m, v.y);
+    m = pk_absmax(m, v.z);
+    return pk_absmax(m, v.w);
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, int64_t n,
                                                    uint32_t* __restrict__ out) {
+  constexpr int kU = FP8Q_KU_A;
+  constexpr int64_t kChunk = (int64_t)kU * kThreads;
   const int64_t per_vec = DT == FP8Q_F32 ? 4 : 8;
   const int64_t nvec = n / per_vec;
   const u32x4* xv = (const u32x4*)x;
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; i + 3 * stride < nvec; i += 4 * stride) {
-    u32x4 v[4];
+  for (int64_t c = blockIdx.x; c * kChunk < nvec; c += gridDim.x) {
+    const int64_t base = c * kChunk + threadIdx.x;
+    u32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(xv + i + u * stride);
+    for (int u = 0; u < kU; ++u)
+      v[u] = base + u * kThreads < nvec ? __builtin_nontemporal_load(xv + base + u * kThreads) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if constexpr (DT == FP8Q_F32) {
-        m = max(m, max(v[u].x & 0x7FFFFFFFu, v[u].y & 0x7FFFFFFFu));
-        m = max(m, max(v[u].z & 0x7FFFFFFFu, v[u].w & 0x7FFFFFFFu));
-      } else {
-        m = pk_absmax(m, v[u].x);
-        m = pk_absmax(m, v[u].y);
-        m = pk_absmax(m, v[u].z);
-        m = pk_absmax(m, v[u].w);
-      }
-    }
-  }
-  for (; i < nvec; i += stride) {
-    u32x4 v = __builtin_nontemporal_load(xv + i);
-    if constexpr (DT == FP8Q_F32) {
-      m = max(m, max(v.x & 0x7FFFFFFFu, v.y & 0x7FFFFFFFu));
-      m = max(m, max(v.z & 0x7FFFFFFFu, v.w & 0x7FFFFFFFu));
-    } else {
-      m = pk_absmax(m, v.x);
-      m = pk_absmax(m, v.y);
-      m = pk_absmax(m, v.z);
-      m = pk_absmax(m, v.w);
-    }
+    for (int u = 0; u < kU; ++u) m = vec_absmax<DT>(m, v[u]);
   }
   if constexpr (DT == FP8Q_BF16) m = pk_fold(m);
   // tail elements (n not a multiple of the vector width)
@@ -101,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
     }
   }
   m = block_max(m);
-  if (threadIdx.x == 0) atomicMax(out, canon_abs_bits(m));
+  if (threadIdx.x == 0) fold_max(out, canon_abs_bits(m));
 }
 
 // ---------------------------------------------------------------- per-tensor
@@ -110,14 +141,10 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
 // vector holding a NaN re-encodes its elements one by one (NaN -> 0x7F),
 // and a scale outside [2^-80, 2^80] (or NaN / zero / Inf) takes IEEE
 // division for every element.
-template <int DT, int FMT>
-__device__ __forceinline__ uint32_t quant4(float a, float b, float c, float d, float s, float r,
-                                           bool fast) {
-  if (fast)
-    return pack4<FMT>(sat<FMT>(div_rn_wide(a, s, r)), sat<FMT>(div_rn_wide(b, s, r)),
-                      sat<FMT>(div_rn_wide(c, s, r)), sat<FMT>(div_rn_wide(d, s, r)));
-  return enc1<FMT>(a / s) | (enc1<FMT>(b / s) << 8) | (enc1<FMT>(c / s) << 16) |
-         (enc1<FMT>(d / s) << 24);
+template <int FMT>
+__device__ __forceinline__ uint32_t quant4_fast(float a, float b, float c, float d, float s, float r) {
+  return pack4<FMT>(sat<FMT>(div_rn_wide(a, s, r)), sat<FMT>(div_rn_wide(b, s, r)),
+                    sat<FMT>(div_rn_wide(c, s, r)), sat<FMT>(div_rn_wide(d, s, r)));
 }
 template <int FMT>
 __device__ __forceinline__ uint32_t quant4_exact(float a, float b, float c, float d, float s) {
@@ -125,47 +152,42 @@ __device__ __forceinline__ uint32_t quant4_exact(float a, float b, float c, floa
          (enc1<FMT>(d / s) << 24);
 }
 
-template <int DT, int FMT>
-__global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restrict__ x, int64_t n,
-                                                           const float* __restrict__ scale,
-                                                           uint8_t* __restrict__ q,
-                                                           uint32_t* __restrict__ amax_acc) {
-  const float s = *scale;
-  const bool fast = scale_ok(s);
-  const float r = 1.0f / s;
-  const int64_t per_vec = DT == FP8Q_F32 ? 4 : 8;
-  const int64_t nvec = n / per_vec;
-  const u32x4* xv = (const u32x4*)x;
+// The stream of one per-tensor quantization.  FAST selects, once for the
+// whole tensor, the corrected-reciprocal division (scale in [2^-80, 2^80])
+// or IEEE division for every element; a vector holding a NaN is re-encoded
+// element by element either way.  Returns the lane's max |x| bit pattern.
+template <int DT, int FMT, bool FAST>
+__device__ __forceinline__ uint32_t tensor_stream(const u32x4* __restrict__ xv, int64_t nvec, float s,
+                                                  float r, uint8_t* __restrict__ q) {
+  constexpr int kU = FP8Q_KU_T;
+  constexpr int64_t kChunk = (int64_t)kU * kThreads;
   uint32_t m = 0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nvec; i0 += 4 * stride) {
-    u32x4 v[4];
+  for (int64_t c = blockIdx.x; c * kChunk < nvec; c += gridDim.x) {
+    const int64_t base = c * kChunk + threadIdx.x;
+    u32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (i0 + u * stride < nvec) v[u] = __builtin_nontemporal_load(xv + i0 + u * stride);
+    for (int u = 0; u < kU; ++u)
+      if (base + u * kThreads < nvec) v[u] = __builtin_nontemporal_load(xv + base + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + u * stride;
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = base + u * kThreads;
       if (i >= nvec) break;
       if constexpr (DT == FP8Q_F32) {
-        uint32_t mv = max(max(v[u].x & 0x7FFFFFFFu, v[u].y & 0x7FFFFFFFu),
-                          max(v[u].z & 0x7FFFFFFFu, v[u].w & 0x7FFFFFFFu));
+        const uint32_t mv = vec_absmax<DT>(0u, v[u]);
         m = max(m, mv);
-        float a = __uint_as_float(v[u].x), b = __uint_as_float(v[u].y);
-        float c = __uint_as_float(v[u].z), d = __uint_as_float(v[u].w);
-        uint32_t w = quant4<DT, FMT>(a, b, c, d, s, r, fast);
-        if (mv > 0x7F800000u) w = quant4_exact<FMT>(a, b, c, d, s);
+        const float a = __uint_as_float(v[u].x), b = __uint_as_float(v[u].y);
+        const float c4 = __uint_as_float(v[u].z), d = __uint_as_float(v[u].w);
+        uint32_t w = FAST ? quant4_fast<FMT>(a, b, c4, d, s, r) : quant4_exact<FMT>(a, b, c4, d, s);
+        if (mv > 0x7F800000u) w = quant4_exact<FMT>(a, b, c4, d, s);
         __builtin_nontemporal_store(w, (uint32_t*)q + i);
       } else {
-        uint32_t pm = pk_absmax(pk_absmax(0u, v[u].x), v[u].y);
-        pm = pk_absmax(pk_absmax(pm, v[u].z), v[u].w);
-        uint32_t mv = pk_fold(pm);
+        const uint32_t mv = pk_fold(vec_absmax<DT>(0u, v[u]));
         m = max(m, mv);
-        float e0 = bf_lo(v[u].x), e1 = bf_hi(v[u].x), e2 = bf_lo(v[u].y), e3 = bf_hi(v[u].y);
-        float e4 = bf_lo(v[u].z), e5 = bf_hi(v[u].z), e6 = bf_lo(v[u].w), e7 = bf_hi(v[u].w);
+        const float e0 = bf_lo(v[u].x), e1 = bf_hi(v[u].x), e2 = bf_lo(v[u].y), e3 = bf_hi(v[u].y);
+        const float e4 = bf_lo(v[u].z), e5 = bf_hi(v[u].z), e6 = bf_lo(v[u].w), e7 = bf_hi(v[u].w);
         u32x2 w;
-        w.x = quant4<DT, FMT>(e0, e1, e2, e3, s, r, fast);
-        w.y = quant4<DT, FMT>(e4, e5, e6, e7, s, r, fast);
+        w.x = FAST ? quant4_fast<FMT>(e0, e1, e2, e3, s, r) : quant4_exact<FMT>(e0, e1, e2, e3, s);
+        w.y = FAST ? quant4_fast<FMT>(e4, e5, e6, e7, s, r) : quant4_exact<FMT>(e4, e5, e6, e7, s);
         if (mv > 0x7F800000u) {
           w.x = quant4_exact<FMT>(e0, e1, e2, e3, s);
           w.y = quant4_exact<FMT>(e4, e5, e6, e7, s);
@@ -174,6 +196,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restric
       }
     }
   }
+  return m;
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restrict__ x, int64_t n,
+                                                           const float* __restrict__ scale,
+                                                           uint8_t* __restrict__ q,
+                                                           uint32_t* __restrict__ amax_acc) {
+  const float s = *scale;
+  const float r = 1.0f / s;
+  const int64_t per_vec = DT == FP8Q_F32 ? 4 : 8;
+  const int64_t nvec = n / per_vec;
+  const u32x4* xv = (const u32x4*)x;
+  uint32_t m = scale_ok(s) ? tensor_stream<DT, FMT, true>(xv, nvec, s, r, q)
+                           : tensor_stream<DT, FMT, false>(xv, nvec, s, r, q);
   if (blockIdx.x == 0) {
     for (int64_t j = nvec * per_vec + threadIdx.x; j < n; j += kThreads) {
       uint32_t b = DT == FP8Q_F32 ? ((const uint32_t*)x)[j]
@@ -184,16 +221,21 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restric
   }
   if (amax_acc) {
     m = block_max(m);
-    if (threadIdx.x == 0) atomicMax(amax_acc, canon_abs_bits(m));
+    if (threadIdx.x == 0) fold_max(amax_acc, canon_abs_bits(m));
   }
 }
 
 // ---------------------------------------------------------------- 1x128
 // Each 16-lane DPP row of a wavefront owns one 128-element block: 16 lanes
 // x 16 bytes is the whole block for bf16, and two such loads for fp32
-// (element offsets 4l and 64+4l).  A wavefront walks groups of four
-// consecutive blocks; each lane keeps kGroups groups in flight.
-static constexpr int kGroups = 4;
+// (element offsets 4l and 64+4l).  A wavefront takes kGroups groups of four
+// consecutive blocks, all loads in flight at once; a workgroup's four
+// wavefronts cover consecutive stretches, so each workgroup streams one
+// contiguous chunk of the (row, block) sequence at a time.
+#ifndef FP8Q_KGROUPS
+#define FP8Q_KGROUPS 4
+#endif
+static constexpr int kGroups = FP8Q_KGROUPS;
 
 template <int DT, int FMT>
 __device__ __forceinline__ void quant_block_regs(const u32x4* v, uint32_t amax_bits, float eps,
@@ -260,24 +302,30 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict
                                                           float* __restrict__ scales, int64_t ld_s) {
   constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
   constexpr int NV = DT == FP8Q_F32 ? 2 : 1;  // 16-byte vectors per lane per block
+  constexpr int64_t kWaveBlocks = 4 * kGroups;               // consecutive blocks per wavefront
+  constexpr int64_t kBlocks = kWaveBlocks * (kThreads / 64);  // per workgroup chunk
   const int lane = threadIdx.x & 63;
-  const int w = lane >> 4, l = lane & 15;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
-                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int rr = lane >> 4, l = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const char* xb = (const char*)x;
-  for (int64_t b0 = wave * 4 * kGroups; b0 < nblocks; b0 += nwaves * 4 * kGroups) {
+  for (int64_t c = blockIdx.x; c * kBlocks < nblocks; c += gridDim.x) {
+    // (row, column block) of the wavefront's first block, then stepped by 4
+    const int64_t b0 = c * kBlocks + wave * kWaveBlocks;  // wave-uniform
+    int64_t rg = b0 / nkb, kg = b0 - rg * nkb;
     u32x4 v[kGroups][NV];
     int64_t row[kGroups], kb[kGroups];
     bool ok[kGroups];
 #pragma unroll
     for (int g = 0; g < kGroups; ++g) {
-      const int64_t bg = b0 + 4 * g;  // wave-uniform
-      int64_t r0 = bg / nkb, k0 = bg - r0 * nkb + w;
+      if (g > 0) {
+        kg += 4;
+        while (kg >= nkb) { kg -= nkb; ++rg; }
+      }
+      int64_t r0 = rg, k0 = kg + rr;
       while (k0 >= nkb) { k0 -= nkb; ++r0; }
       row[g] = r0;
       kb[g] = k0;
-      ok[g] = bg + w < nblocks;
+      ok[g] = b0 + 4 * g + rr < nblocks;
       if (ok[g]) {
         const u32x4* p = (const u32x4*)(xb + (r0 * ldx + 128 * k0) * esz);
 #pragma unroll
@@ -434,21 +482,23 @@ __device__ __forceinline__ float canon_nan(float f) {
   return f != f ? __uint_as_float(0x7FC00000u) : f;
 }
 
-// Work unit: (row, 4096-column chunk); each thread handles 4 groups of 4
-// codes (one dword load; one 16-byte fp32 or 8-byte bf16 store each).
+// Work unit: (row, chunk of 1024*FP8Q_KU_D columns); each thread handles
+// FP8Q_KU_D groups of 4 codes, lanes on consecutive dwords (one dword load;
+// one 16-byte fp32 or 8-byte bf16 store each).
 template <int FMT, int GRAN, int ODT>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ q, int64_t rows,
                                                       int64_t cols, int64_t ldq,
                                                       const float* __restrict__ scales,
                                                       int64_t ld_s, void* __restrict__ y,
                                                       int64_t ldy) {
-  const int64_t nchunk = (cols + 4095) / 4096;
+  constexpr int64_t CW = 1024 * FP8Q_KU_D;
+  const int64_t nchunk = (cols + CW - 1) / CW;
   const int64_t units = rows * nchunk;
   for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
     const int64_t r = u / nchunk, ch = u - r * nchunk;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int64_t c = ch * 4096 + g * 1024 + 4 * threadIdx.x;
+    for (int g = 0; g < FP8Q_KU_D; ++g) {
+      const int64_t c = ch * CW + g * 1024 + 4 * threadIdx.x;
       if (c >= cols) break;
       float s;
       if constexpr (GRAN == FP8Q_GRAN_TENSOR) s = scales[0];
@@ -481,18 +531,20 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
 }
 
 // ---------------------------------------------------------------- launches
-static int grid_for(int64_t work_items, int per_cu) {
+// Persistent grid for chunked streams: up to per_cu workgroups per CU.
+static int chunk_grid(int64_t chunks, int per_cu) {
   const int64_t cap = (int64_t)device_cu_count() * per_cu;
-  int64_t g = (work_items + kThreads - 1) / kThreads;
-  if (g > cap) g = cap;
+  const int64_t g = chunks < cap ? chunks : cap;
   return g < 1 ? 1 : (int)g;
 }
+
 
 int launch_amax(const void* x, int dt, int64_t n, float* amax, hipStream_t st) {
   hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, st, (uint32_t*)amax, 0u);
   if (int e = check_launch("amax reset")) return e;
   const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
-  const int grid = grid_for(nvec / 4, 8);
+  const int64_t ch = (int64_t)FP8Q_KU_A * kThreads;
+  const int grid = chunk_grid((nvec + ch - 1) / ch, FP8Q_G_A);
   if (dt == FP8Q_F32)
     hipLaunchKernelGGL(k_amax<FP8Q_F32>, dim3(grid), dim3(kThreads), 0, st, x, n, (uint32_t*)amax);
   else
@@ -510,7 +562,8 @@ static void launch_qt(int grid, const void* x, int64_t n, const float* scale, ui
 int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const float* scale, uint8_t* q,
                            float* amax_acc, hipStream_t st) {
   const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
-  const int grid = grid_for(nvec / 4, 8);
+  const int64_t ch = (int64_t)FP8Q_KU_T * kThreads;
+  const int grid = chunk_grid((nvec + ch - 1) / ch, FP8Q_G_T);
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st);
   else if (dt == FP8Q_F32) launch_qt<FP8Q_F32, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st);
   else if (fmt == FP8Q_E4M3FN) launch_qt<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st);
@@ -529,9 +582,9 @@ int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int
                           float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                           hipStream_t st) {
   const int64_t nkb = cols / 128, nblocks = rows * nkb;
-  // one wavefront handles 4*kGroups blocks per pass
-  const int64_t waves = (nblocks + 4 * kGroups - 1) / (4 * kGroups);
-  const int grid = grid_for(waves * 64, 8);
+  // one workgroup handles 4*kGroups blocks per wavefront per chunk
+  const int64_t per_chunk = 4 * kGroups * (kThreads / 64);
+  const int grid = chunk_grid((nblocks + per_chunk - 1) / per_chunk, FP8Q_G_1);
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1<FP8Q_F32, FP8Q_E4M3FN>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
   else if (dt == FP8Q_F32) launch_q1<FP8Q_F32, FP8Q_E5M2>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
   else if (fmt == FP8Q_E4M3FN) launch_q1<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
@@ -572,9 +625,9 @@ int launch_scaler_update(fp8q_scaler* s, float* amax, hipStream_t st) {
 template <int FMT, int GRAN, int ODT>
 static void launch_dq(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* scales,
                       int64_t ld_s, void* y, int64_t ldy, hipStream_t st) {
-  const int64_t units = rows * ((cols + 4095) / 4096);
+  const int64_t units = rows * ((cols + 1024 * FP8Q_KU_D - 1) / (1024 * FP8Q_KU_D));
   int64_t grid = units;
-  const int64_t cap = (int64_t)device_cu_count() * 16;
+  const int64_t cap = (int64_t)device_cu_count() * FP8Q_G_D;
   if (grid > cap) grid = cap;
   hipLaunchKernelGGL((k_dequant<FMT, GRAN, ODT>), dim3((unsigned)grid), dim3(kThreads), 0, st, q, rows,
                      cols, ldq, scales, ld_s, y, ldy);
