@@ -16,17 +16,22 @@ Inputs rotate over several buffers so repeated reads are not served from
 the 256 MB last-level cache.
 
 `value` is the step's throughput in TFLOP/s: the layer GEMM's 2*M*N*K per
-step over the step time.  Per-kernel figures (GB/s for the quantizers,
-TFLOP/s for the GEMM, each with its roofline fraction) are measured with
-events around each launch on the launch stream.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step and extrapolates per unit.
+step over the step time.  All launches are captured into HIP graphs and
+replayed (one graph per input rotation), so host launch costs stay out of
+the timings; per-kernel figures (GB/s for the quantizers, TFLOP/s for the
+GEMM, each with its roofline fraction) come from graphs of repeated
+launches of one kernel, timed with events on the replay stream.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same step
+and extrapolates per unit.
 Prints one JSON line on stdout; progress goes to stderr.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -44,6 +49,14 @@ LM, LN, LK = 16384, 18432, 7168  # LLM layer: X [M,K] bf16, W [N,K], C [M,N] bf1
 WINDOW = 16
 N_ROT = 8                        # rotating delayed-scaling buffers per tensor
 X_ROT = 2
+COPY_ELEMS = 1 << 28             # fp32 copy reference: 1 GiB read + 1 GiB written
+
+# HBM bytes per GEMM launch, from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
+# passes over this same command, scaled by what the counters read for the
+# copy reference; valid only for the kernel source the counters were taken on.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_blockscaled_16384x18432x7168_hbm_traffic.md")
+GEMM_SOURCES = ("block_scaled_precision_amax_amd/csrc/fp8q_gemm.hip",
+                "block_scaled_precision_amax_amd/csrc/fp8q_internal.h")
 
 
 def log(*a):
@@ -58,7 +71,30 @@ def algorithmic():
         "dequantize_bytes": n + 2 * n + 4,                  # codes read, bf16 written, scale
         "quantize_1x128_bytes": nx * 2 + nx + 4 * nx // 128,  # bf16 read, codes + scales written
         "gemm_flop": 2 * LM * LN * LK,
+        # codes of A and B, their scales, bf16 C
+        "gemm_bytes": LM * LK + LN * LK + 4 * (LM * (LK // 128) + (LN // 128) * (LK // 128)) + 2 * LM * LN,
     }
+
+
+def gemm_source_sha256() -> str:
+    h = hashlib.sha256()
+    for p in GEMM_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Counter-measured HBM bytes per GEMM launch, or None when the summary is
+    missing or was taken on different GEMM source."""
+    try:
+        with open(TRAFFIC_SUMMARY) as f:
+            fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), re.M))
+    except OSError:
+        return None
+    if fields.get("source_sha256") != gemm_source_sha256() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def run_gpu(steps: int, warmup: int):
@@ -96,59 +132,89 @@ def run_gpu(steps: int, warmup: int):
     sc_g = st_g.data_ptr() + fq.SCALER_SCALE_OFFSET
     torch.cuda.synchronize()
 
-    names = ["quantize_tensor_x", "quantize_tensor_g", "dequantize_x", "scaler_updates", "quantize_1x128",
-             "gemm"]
-    ev = {k: [] for k in names}
+    def step(t: int):
+        x, g, X = xs[t % N_ROT], gs[t % N_ROT], Xs[t % X_ROT]
+        fq.fp8q_quantize_tensor(x, n, fq.E4M3FN, sc_x, qx, am_x)
+        fq.fp8q_quantize_tensor(g, n, fq.E5M2, sc_g, qg, am_g)
+        fq.fp8q_dequantize(qx, fq.E4M3FN, 1, n, n, sc_x, fq.GRAN_TENSOR, 1, xhat, n)
+        fq.fp8q_delayed_scaler_update(st_x, am_x)
+        fq.fp8q_delayed_scaler_update(st_g, am_g)
+        fq.fp8q_quantize_1x128(X, LM, LK, LK, fq.E4M3FN, 1e-12, qX, LK, sX, LK // 128)
+        fq.fp8q_gemm_blockscaled(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW, fq.GRAN_128x128,
+                                 LK // 128, 1, C, LN, LM, LN, LK)
+
+    # Every launch is captured into HIP graphs and replayed: a Python launch
+    # costs about as much host time as one of the quantizer kernels runs, so
+    # eager launches would measure the host.  One graph per input rotation.
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        step(0)  # one eager pass before capture
+    torch.cuda.synchronize()
+    period = N_ROT  # multiple of X_ROT
+    graphs = []
+    for t in range(period):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            step(t)
+        graphs.append(gr)
 
     def E():
         e = torch.cuda.Event(enable_timing=True)
         e.record()
         return e
 
-    def step(t: int, timed: bool):
-        x, g, X = xs[t % N_ROT], gs[t % N_ROT], Xs[t % X_ROT]
-        marks = [E()] if timed else None
-        fq.fp8q_quantize_tensor(x, n, fq.E4M3FN, sc_x, qx, am_x)
-        if timed: marks.append(E())
-        fq.fp8q_quantize_tensor(g, n, fq.E5M2, sc_g, qg, am_g)
-        if timed: marks.append(E())
-        fq.fp8q_dequantize(qx, fq.E4M3FN, 1, n, n, sc_x, fq.GRAN_TENSOR, 1, xhat, n)
-        if timed: marks.append(E())
-        fq.fp8q_delayed_scaler_update(st_x, am_x)
-        fq.fp8q_delayed_scaler_update(st_g, am_g)
-        if timed: marks.append(E())
-        fq.fp8q_quantize_1x128(X, LM, LK, LK, fq.E4M3FN, 1e-12, qX, LK, sX, LK // 128)
-        if timed: marks.append(E())
-        fq.fp8q_gemm_blockscaled(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW, fq.GRAN_128x128,
-                                 LK // 128, 1, C, LN, LM, LN, LK)
-        if timed:
-            marks.append(E())
-            for k, a, b in zip(names, marks[:-1], marks[1:]):
-                ev[k].append((a, b))
-
     log(f"warmup {warmup} steps ...")
     for t in range(warmup):
-        step(t, False)
+        graphs[t % period].replay()
     torch.cuda.synchronize()
     log(f"timing {steps} steps ...")
     t0 = time.perf_counter()
+    e0 = E()
     for t in range(warmup, warmup + steps):
-        step(t, True)
+        graphs[t % period].replay()
+    e1 = E()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in ev.items()}
-    # the FP8-MFMA GEMM path on the same operands, outside the timed steps
-    fast = []
-    for t in range(max(steps, 3)):
+    gpu_ms = e0.elapsed_time(e1) / steps
+
+    # per-kernel averages: a graph of `reps` launches of one kernel, replayed
+    def per_launch(launch, reps):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=cap):
+            for r in range(reps):
+                launch(r)
+        gr.replay()
+        torch.cuda.synchronize()
         a = E()
-        fq.fp8q_gemm_blockscaled_fast(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW, fq.GRAN_128x128,
-                                      LK // 128, 1, C, LN, LM, LN, LK)
-        fast.append((a, E()))
-    torch.cuda.synchronize()
-    per["gemm_fast"] = sum(a.elapsed_time(b) for a, b in fast[1:]) / len(fast[1:])
-    first = ev[names[0]][0][0]
-    last = ev[names[-1]][-1][1]
-    gpu_ms = first.elapsed_time(last) / steps
+        gr.replay()
+        b = E()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    log("per-kernel timing ...")
+    am_tmp = torch.zeros(1, dtype=torch.float32, device=dev)
+    st_tmp = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
+    fq.fp8q_delayed_scaler_init(st_tmp, WINDOW, 448.0, 1e-12, 1.0)
+    per = {
+        "quantize_tensor_x": per_launch(lambda r: fq.fp8q_quantize_tensor(xs[r % N_ROT], n, fq.E4M3FN, sc_x, qx, am_tmp), 16),
+        "quantize_tensor_g": per_launch(lambda r: fq.fp8q_quantize_tensor(gs[r % N_ROT], n, fq.E5M2, sc_g, qg, am_tmp), 16),
+        "dequantize_x": per_launch(lambda r: fq.fp8q_dequantize(qx, fq.E4M3FN, 1, n, n, sc_x, fq.GRAN_TENSOR, 1, xhat, n), 16),
+        "scaler_update": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_tmp, am_tmp), 16),
+        "quantize_1x128": per_launch(lambda r: fq.fp8q_quantize_1x128(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, 1e-12, qX, LK,
+                                                                       sX, LK // 128), 8),
+        "gemm": per_launch(lambda r: fq.fp8q_gemm_blockscaled(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW,
+                                                              fq.GRAN_128x128, LK // 128, 1, C, LN, LM, LN, LK), 4),
+        "gemm_fast": per_launch(lambda r: fq.fp8q_gemm_blockscaled_fast(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN,
+                                                                        LK, sW, fq.GRAN_128x128, LK // 128, 1, C, LN, LM,
+                                                                        LN, LK), 4),
+    }
+    # Copy reference: a plain elementwise pass (fp32 negation) over 1 GiB,
+    # the yardstick for the streaming kernels and the calibration of the
+    # HBM byte counters.
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    per["copy_reference"] = per_launch(lambda r: torch.neg(src, out=dst), 8)
+    del src, dst
     inputs = {"ds": (xs[0], gs[0]), "X": Xs[0], "qW": qW, "sW": sW}
     return per, gpu_ms, wall * 1e3 / steps, inputs
 
@@ -233,6 +299,8 @@ def main():
     q_g = gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_g"])
     q_1 = gbps(alg["quantize_1x128_bytes"], per["quantize_1x128"])
     dq = gbps(alg["dequantize_bytes"], per["dequantize_x"])
+    cp = gbps(8 * COPY_ELEMS, per["copy_reference"])
+    traffic = measured_traffic()
     out = {
         "metric": "quantize GB/s + block-scaled FP8 GEMM TFLOPS, % of HBM / FP8-MFMA peak",
         "value": round(value, 2),
@@ -255,7 +323,8 @@ def main():
         "roofline": {
             "bound": "mfma", "kernel": "gemm_blockscaled", "mfma_dtype": "bf16 (FP8 codes decoded exactly)",
             "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+            "traffic_unit": "bytes per launch", "algorithmic_bytes": alg["gemm_bytes"],
         },
         "kernels": {
             "gemm_blockscaled": {"ms": round(per["gemm"], 4), "TFLOP/s": round(gemm_tflops, 2),
@@ -272,7 +341,10 @@ def main():
                                           "frac_hbm": round(q_g / HBM_PEAK_GBPS, 4)},
             "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
                                 "frac_hbm": round(dq / HBM_PEAK_GBPS, 4)},
-            "scaler_update_x2": {"ms": round(per["scaler_updates"], 4)},
+            "scaler_update": {"ms": round(per["scaler_update"], 4)},
+            "copy_reference_fp32": {"ms": round(per["copy_reference"], 4), "GB/s": round(cp, 1),
+                                    "frac_hbm": round(cp / HBM_PEAK_GBPS, 4),
+                                    "note": "torch elementwise pass, 1 GiB in + 1 GiB out: attainable streaming rate"},
         },
     }
     if not args.no_cpu_baseline:
