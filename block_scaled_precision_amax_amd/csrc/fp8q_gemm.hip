@@ -50,11 +50,19 @@ static constexpr int kGemmThreads = 512;  // eight wavefronts, 2 x 4
 // exact path: 4 x 4 tiles (64 x 64, 128 x 256), which leaves room for the
 // decoded bf16 fragments in the 256 registers a lane has at two
 // wavefronts per SIMD.
+//
+// LDS stages: the exact path's 48 KB per K block allows three (two blocks
+// in flight while one is computed); the FP8 path's 64 KB per block allows
+// two.
 template <bool FAST>
 struct Cfg {
   static constexpr int WGM = 2, WGN = 4;
   static constexpr int TI = FAST ? 8 : 4, TJ = 4;
   static constexpr int BM = WGM * TI * 16, BN = WGN * TJ * 16;
+  static constexpr int NST = FAST ? 2 : 3;
+  // global-to-LDS loads one wavefront issues per K block: A and B code
+  // tiles (1 KB each) and one for the tile rows' A scales
+  static constexpr int NLOAD = BM / 64 + BN / 64 + 1;
 };
 
 // Two FP8 codes (bytes 0-1 or 2-3 of w) -> two bf16, exact.
@@ -128,14 +136,35 @@ __device__ __forceinline__ void dma_offsets(uint32_t* off, int64_t ld, int64_t r
   }
 }
 
+// Global-to-LDS copies are issued as inline assembly.  Issued through the
+// builtin, the compiler sees LDS writes it cannot tell apart from the
+// fragment reads of the stage being computed and makes every wavefront
+// wait for the copy before its first LDS read, which serializes copy and
+// compute.  Here the kernel alone orders them: explicit vmcnt waits plus a
+// workgroup barrier before a stage is read.  M0 holds the LDS destination
+// of lane 0; lane l writes `size` bytes at M0 + l*size.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const uint8_t* sbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const float* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :
+               : "s"(lds_addr), "v"(gptr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr_of(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 // Issues the loads of one tile: base is the operand advanced to the K block.
 template <int R>
 __device__ __forceinline__ void dma_tile(uint8_t* lds, const uint8_t* base, const uint32_t* off, int wave) {
 #pragma unroll
   for (int u = 0; u < R / 64; ++u)
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + off[u]),
-                                     (__attribute__((address_space(3))) void*)(lds + (wave * (R / 64) + u) * 1024),
-                                     16, 0, 0);
+    lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds + (wave * (R / 64) + u) * 1024)), base, off[u]);
 }
 
 // One workgroup of eight wavefronts computes a BM x BN tile of C; wavefront
@@ -154,10 +183,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     int64_t sB_sn, int64_t sB_skb, void* __restrict__ C, int64_t ldc, int64_t M, int64_t N,
     int64_t K, int64_t ntm, int64_t ntn) {
   using G = Cfg<FAST>;
-  constexpr int BM = G::BM, BN = G::BN, TI = G::TI, TJ = G::TJ;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2][BM * BK];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2][BN * BK];
-  __shared__ __attribute__((aligned(16))) float lds_sa[2][BM];  // 1x128 A scales of the tile's rows
+  constexpr int BM = G::BM, BN = G::BN, TI = G::TI, TJ = G::TJ, NST = G::NST;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[NST][BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b[NST][BN * BK];
+  __shared__ __attribute__((aligned(16))) float lds_sa[NST][BM];  // 1x128 A scales of the tile's rows
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,8 +196,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t nkb = K / BK;
 
-  const float* sa_row = sA + ((m0 + tid < M) ? m0 + tid : M - 1) * sA_sm;
-  float rsa = 0.0f;
+  // A scales: wavefront w stages rows w*BM/8 .. +BM/8 of the tile, one per
+  // lane (rows past M read the last row)
+  constexpr int SA_LANES = BM / 8;
+  const int64_t sa_r = m0 + wave * SA_LANES + (lane < SA_LANES ? lane : 0);
+  const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
   uint32_t a_off[BM / 64], b_off[BN / 64];
   dma_offsets<BM>(a_off, lda, m0, M, wave, lane);
   dma_offsets<BN>(b_off, ldb, n0, N, wave, lane);
@@ -193,8 +225,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const float* sb_blk = sB + (wcol0 >> 7) * sB_sn;
 
   // P_kb of every MFMA tile of the wavefront, folded into acc
-  auto compute = [&](int64_t kb) {
-    const int s = (int)(kb & 1);
+  auto compute = [&](int64_t kb, int s) {
     // the B scale(s) of this wavefront's columns
     float sbv[TJ];
     float sbw = 1.0f;
@@ -342,24 +373,54 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
       for (int e = 0; e < 4; ++e) fold(TI - 1, j, e, pp[j][e], cp);
   };
 
-  dma_tile<BM>(lds_a[0], A, a_off, wave);
-  dma_tile<BN>(lds_b[0], B, b_off, wave);
-  if (tid < BM) lds_sa[0][tid] = sa_row[0];
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Everything one wavefront copies into LDS stage st for K block kb.
+  auto stage_block = [&](int64_t kb, int st) {
+    dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+    dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
+    if (lane < SA_LANES)
+      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+  };
+  auto next_stage = [](int st) { return st + 1 == NST ? 0 : st + 1; };
+
+  // Prologue: the first NST-1 blocks in flight, wait for block 0.
+  stage_block(0, 0);
+  if constexpr (NST == 3) {
+    if (nkb > 1) {
+      stage_block(1, 1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::NLOAD) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   __syncthreads();
 
-  // steady state: copy block kb+1 while computing block kb, no branches
-  for (int64_t kb = 0; kb + 1 < nkb; ++kb) {
-    const int s = (int)(kb & 1);
-    dma_tile<BM>(lds_a[s ^ 1], A + (kb + 1) * BK, a_off, wave);
-    dma_tile<BN>(lds_b[s ^ 1], B + (kb + 1) * BK, b_off, wave);
-    if (tid < BM) rsa = sa_row[(kb + 1) * sA_skb];
-    compute(kb);
-    if (tid < BM) lds_sa[s ^ 1][tid] = rsa;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Steady state, no branches: copy block kb+NST-1 while computing block
+  // kb, then wait for block kb+1 only (the newer copies stay in flight).
+  int st = 0;
+  int64_t kb = 0;
+  for (; kb + NST - 1 < nkb; ++kb) {
+    int sn = st;
+#pragma unroll
+    for (int u = 0; u < NST - 1; ++u) sn = next_stage(sn);
+    stage_block(kb + NST - 1, sn);
+    compute(kb, st);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::NLOAD * (NST - 2)) : "memory");
     __syncthreads();
+    st = next_stage(st);
   }
-  compute(nkb - 1);
+  // Drain: every remaining block is already in flight.
+  if constexpr (NST == 3) {
+    if (kb + 1 < nkb) {
+      compute(kb, st);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      st = next_stage(st);
+      ++kb;
+    }
+  }
+  compute(kb, st);
 
   // ---- epilogue
 #pragma unroll
