@@ -208,6 +208,52 @@ def run_gpu(steps: int, warmup: int):
                                                                         LK, sW, fq.GRAN_128x128, LK // 128, 1, C, LN, LM,
                                                                         LN, LK), 4),
     }
+    # The other GEMM shapes (per-kernel figures only, not part of the step):
+    # 4096^3 with 1x128 A and 128x128 B scales, bf16 out; and the backward
+    # GEMMs of a 4096-wide layer over 16384 tokens, fp32 out: dgrad (E5M2
+    # gradients x E4M3 transposed weight, 128x128 B scales) and wgrad (both
+    # operands 1x128 along the tokens).  Inputs are quantized by the library
+    # once, untimed.
+    inputs = {"ds": (xs[0], gs[0]), "X": Xs[0], "qW": qW, "sW": sW}
+    log("other GEMM shapes ...")
+    del xs, gs
+    torch.cuda.empty_cache()
+
+    def q1x128(x, fmt):
+        r, c = x.shape
+        q = torch.empty(r, c, dtype=torch.uint8, device=dev)
+        sc = torch.empty(r, c // 128, dtype=torch.float32, device=dev)
+        fq.fp8q_quantize_1x128(x, r, c, c, fmt, 1e-12, q, c, sc, c // 128)
+        return q, sc
+
+    def q128(x, fmt):
+        r, c = x.shape
+        q = torch.empty(r, c, dtype=torch.uint8, device=dev)
+        sc = torch.empty(r // 128, c // 128, dtype=torch.float32, device=dev)
+        fq.fp8q_quantize_128x128(x, r, c, c, fmt, 1e-12, q, c, sc, c // 128)
+        return q, sc
+
+    def gemm_ms(qa, fa, sa, qb, fb, sb, gb, out_dtype):
+        Mg, Kg = qa.shape
+        Ng = qb.shape[0]
+        Cg = torch.empty(Mg, Ng, dtype=out_dtype, device=dev)
+        return per_launch(lambda r: fq.fp8q_gemm_blockscaled(qa, fa, Kg, sa, sa.shape[1], 1, qb, fb, Kg, sb, gb,
+                                                             sb.shape[1], 1, Cg, Ng, Mg, Ng, Kg), 8)
+
+    a3, sa3 = q1x128(W.activation(4096, 4096, seed=3, factor=100.0, device=dev), fq.E4M3FN)
+    b3, sb3 = q128(W.weight(4096, 4096, seed=30, device=dev), fq.E4M3FN)
+    per["gemm_4096"] = gemm_ms(a3, fq.E4M3FN, sa3, b3, fq.E4M3FN, sb3, fq.GRAN_128x128, torch.bfloat16)
+    del a3, sa3, b3, sb3
+    dy, sdy = q1x128(W.gradient(16384, 4096, seed=5, device=dev), fq.E5M2)
+    wt, swt = q128(W.weight(4096, 4096, seed=50, device=dev), fq.E4M3FN)
+    per["gemm_dgrad"] = gemm_ms(dy, fq.E5M2, sdy, wt, fq.E4M3FN, swt, fq.GRAN_128x128, torch.float32)
+    del dy, sdy, wt, swt
+    dyt, sdyt = q1x128(W.gradient(4096, 16384, seed=51, device=dev), fq.E5M2)
+    xt, sxt = q1x128(W.normal((4096, 16384), seed=52, device=dev), fq.E4M3FN)
+    per["gemm_wgrad"] = gemm_ms(dyt, fq.E5M2, sdyt, xt, fq.E4M3FN, sxt, fq.GRAN_1x128, torch.float32)
+    del dyt, sdyt, xt, sxt
+    torch.cuda.empty_cache()
+
     # Copy reference: a plain elementwise pass (fp32 negation) over 1 GiB,
     # the yardstick for the streaming kernels and the calibration of the
     # HBM byte counters.
@@ -215,7 +261,6 @@ def run_gpu(steps: int, warmup: int):
     dst = torch.empty_like(src)
     per["copy_reference"] = per_launch(lambda r: torch.neg(src, out=dst), 8)
     del src, dst
-    inputs = {"ds": (xs[0], gs[0]), "X": Xs[0], "qW": qW, "sW": sW}
     return per, gpu_ms, wall * 1e3 / steps, inputs
 
 
@@ -293,6 +338,11 @@ def main():
     def gbps(bytes_, ms):
         return bytes_ / (ms * 1e-3) / 1e9
 
+    def gemm_entry(ms, m, n, k, what):
+        tf = 2.0 * m * n * k / (ms * 1e-3) / 1e12
+        return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+                "operands": what}
+
     gemm_tflops = alg["gemm_flop"] / (per["gemm"] * 1e-3) / 1e12
     fast_tflops = alg["gemm_flop"] / (per["gemm_fast"] * 1e-3) / 1e12
     q_t = gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_x"])
@@ -342,6 +392,12 @@ def main():
             "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
                                 "frac_hbm": round(dq / HBM_PEAK_GBPS, 4)},
             "scaler_update": {"ms": round(per["scaler_update"], 4)},
+            "gemm_blockscaled_4096x4096x4096": gemm_entry(per["gemm_4096"], 4096, 4096, 4096,
+                                                          "E4M3FN x E4M3FN, 1x128 A / 128x128 B scales, bf16 out"),
+            "gemm_blockscaled_dgrad_16384x4096x4096": gemm_entry(per["gemm_dgrad"], 16384, 4096, 4096,
+                                                                 "E5M2 x E4M3FN, 1x128 A / 128x128 B scales, fp32 out"),
+            "gemm_blockscaled_wgrad_4096x4096x16384": gemm_entry(per["gemm_wgrad"], 4096, 4096, 16384,
+                                                                 "E5M2 x E4M3FN, 1x128 A and B scales, fp32 out"),
             "copy_reference_fp32": {"ms": round(per["copy_reference"], 4), "GB/s": round(cp, 1),
                                     "frac_hbm": round(cp / HBM_PEAK_GBPS, 4),
                                     "note": "torch elementwise pass, 1 GiB in + 1 GiB out: attainable streaming rate"},

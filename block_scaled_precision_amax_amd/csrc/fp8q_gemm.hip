@@ -61,7 +61,8 @@ struct Cfg {
   static constexpr int BM = WGM * TI * 16, BN = WGN * TJ * 16;
   static constexpr int NST = FAST ? 2 : 3;
   // global-to-LDS loads one wavefront issues per K block: A and B code
-  // tiles (1 KB each) and one for the tile rows' A scales
+  // tiles (1 KB each) and one for the tile rows' A scales (plus one for the
+  // columns' B scales when those are 1x128)
   static constexpr int NLOAD = BM / 64 + BN / 64 + 1;
 };
 
@@ -187,6 +188,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[NST][BM * BK];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[NST][BN * BK];
   __shared__ __attribute__((aligned(16))) float lds_sa[NST][BM];  // 1x128 A scales of the tile's rows
+  // with 1x128 B scales, those of the tile's columns
+  constexpr bool SB_COLS = GB == FP8Q_GRAN_1x128;
+  __shared__ __attribute__((aligned(16))) float lds_sb[NST][SB_COLS ? BN : 1];
+  constexpr int NL = G::NLOAD + (SB_COLS ? 1 : 0);  // loads per wavefront per K block
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,13 +221,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int lr = lane & 15, lq = lane >> 4;
   const int a_row0 = (wm * TI * 16 + lr) * BK, b_row0 = (wn * TJ * 16 + lr) * BK;
   const int64_t wcol0 = n0 + wn * TJ * 16;  // first column of this wavefront
-  uint32_t col_s[TJ];
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int64_t col = wcol0 + 16 * j + lr;
-    col_s[j] = (uint32_t)((col < N ? col : N - 1) * sB_sn);
-  }
   const float* sb_blk = sB + (wcol0 >> 7) * sB_sn;
+  // 1x128 B scales: wavefront w stages columns w*BN/8 .. +BN/8 of the tile
+  constexpr int SB_LANES = BN / 8;
+  const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);
+  const float* sb_col = sB + (sb_c < N ? sb_c : N - 1) * sB_sn;
 
   // P_kb of every MFMA tile of the wavefront, folded into acc
   auto compute = [&](int64_t kb, int s) {
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
       sbw = sb_blk[kb * sB_skb];
     } else {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sbv[j] = (sB + kb * sB_skb)[col_s[j]];
+      for (int j = 0; j < TJ; ++j) sbv[j] = lds_sb[s][wn * TJ * 16 + 16 * j + lr];
     }
     const uint8_t* la = lds_a[s] + a_row0;
     const uint8_t* lb = lds_b[s] + b_row0;
@@ -379,6 +382,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
     if (lane < SA_LANES)
       lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+    if constexpr (SB_COLS) {
+      if (lane < SB_LANES)
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + wave * SB_LANES)), sb_col + kb * sB_skb);
+    }
   };
   auto next_stage = [](int st) { return st + 1 == NST ? 0 : st + 1; };
 
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   if constexpr (NST == 3) {
     if (nkb > 1) {
       stage_block(1, 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::NLOAD) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -406,7 +413,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     for (int u = 0; u < NST - 1; ++u) sn = next_stage(sn);
     stage_block(kb + NST - 1, sn);
     compute(kb, st);
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(G::NLOAD * (NST - 2)) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL * (NST - 2)) : "memory");
     __syncthreads();
     st = next_stage(st);
   }
