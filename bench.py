@@ -249,9 +249,15 @@ def run_gpu(steps: int, warmup: int):
     per["gemm_dgrad"] = gemm_ms(dy, fq.E5M2, sdy, wt, fq.E4M3FN, swt, fq.GRAN_128x128, torch.float32)
     del dy, sdy, wt, swt
     dyt, sdyt = q1x128(W.gradient(4096, 16384, seed=51, device=dev), fq.E5M2)
-    xt, sxt = q1x128(W.normal((4096, 16384), seed=52, device=dev), fq.E4M3FN)
+    # the activations' operand comes from bf16 X [tokens, features] through
+    # the transposed 1x128 quantizer (timed here as well)
+    Xa = W.normal((16384, 4096), seed=52, device=dev, dtype=torch.bfloat16)
+    xt = torch.empty(4096, 16384, dtype=torch.uint8, device=dev)
+    sxt = torch.empty(4096, 128, dtype=torch.float32, device=dev)
+    per["quantize_1x128_t"] = per_launch(lambda r: fq.fp8q_quantize_1x128_t(Xa, 16384, 4096, 4096, fq.E4M3FN, 1e-12,
+                                                                            xt, 16384, sxt, 128), 16)
     per["gemm_wgrad"] = gemm_ms(dyt, fq.E5M2, sdyt, xt, fq.E4M3FN, sxt, fq.GRAN_1x128, torch.float32)
-    del dyt, sdyt, xt, sxt
+    del dyt, sdyt, xt, sxt, Xa
     torch.cuda.empty_cache()
 
     # Copy reference: a plain elementwise pass (fp32 negation) over 1 GiB,
@@ -392,6 +398,11 @@ def main():
             "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
                                 "frac_hbm": round(dq / HBM_PEAK_GBPS, 4)},
             "scaler_update": {"ms": round(per["scaler_update"], 4)},
+            "quantize_1x128_t_bf16_16384x4096": {
+                "ms": round(per["quantize_1x128_t"], 4),
+                "GB/s": round(gbps(16384 * 4096 * (3 + 4 / 128), per["quantize_1x128_t"]), 1),
+                "frac_hbm": round(gbps(16384 * 4096 * (3 + 4 / 128), per["quantize_1x128_t"]) / HBM_PEAK_GBPS, 4),
+                "note": "codes of the transpose, 1x128 along tokens (weight-gradient operand)"},
             "gemm_blockscaled_4096x4096x4096": gemm_entry(per["gemm_4096"], 4096, 4096, 4096,
                                                           "E4M3FN x E4M3FN, 1x128 A / 128x128 B scales, bf16 out"),
             "gemm_blockscaled_dgrad_16384x4096x4096": gemm_entry(per["gemm_dgrad"], 16384, 4096, 4096,

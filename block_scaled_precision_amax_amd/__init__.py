@@ -31,6 +31,7 @@ SYMBOLS = (
     "fp8q_amax",
     "fp8q_quantize_tensor",
     "fp8q_quantize_1x128",
+    "fp8q_quantize_1x128_t",
     "fp8q_quantize_128x128",
     "fp8q_delayed_scaler_init",
     "fp8q_delayed_scaler_update",
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
             "fp8q_amax": (i32, [vp, i32, i64, vp, vp]),
             "fp8q_quantize_tensor": (i32, [vp, i32, i64, i32, vp, vp, vp, vp]),
             "fp8q_quantize_1x128": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, vp]),
+            "fp8q_quantize_1x128_t": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, vp]),
             "fp8q_quantize_128x128": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, vp]),
             "fp8q_delayed_scaler_init": (i32, [vp, i32, f32, f32, f32, vp]),
             "fp8q_delayed_scaler_update": (i32, [vp, vp, vp]),
@@ -143,6 +145,11 @@ def fp8q_quantize_tensor(x, n, f, scale, q, amax_acc=None, stream=None) -> None:
 def fp8q_quantize_1x128(x, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, stream=None) -> None:
     _check(lib().fp8q_quantize_1x128(_ptr(x), _dt(x), rows, cols, ldx, f, eps, _ptr(q), ldq, _ptr(scales),
                                      ld_s, _stream(stream, x)))
+
+
+def fp8q_quantize_1x128_t(x, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, stream=None) -> None:
+    _check(lib().fp8q_quantize_1x128_t(_ptr(x), _dt(x), rows, cols, ldx, f, eps, _ptr(q), ldq, _ptr(scales),
+                                       ld_s, _stream(stream, x)))
 
 
 def fp8q_quantize_128x128(x, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, stream=None) -> None:

@@ -119,6 +119,25 @@ int fp8q_quantize_1x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols
   return launch_quantize_1x128(x, dt, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, S(stream));
 }
 
+int fp8q_quantize_1x128_t(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                          fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
+                          int64_t ld_s, void* stream) {
+  const char* fn = "quantize_1x128_t";
+  if (!x || !q || !scales) return fail(FP8Q_EINVAL, "%s: null pointer", fn);
+  if (!valid_dt(dt) || !valid_fmt(f)) return fail(FP8Q_EINVAL, "%s: bad dtype or format", fn);
+  if (rows <= 0 || cols <= 0) return fail(FP8Q_EINVAL, "%s: rows and cols must be positive", fn);
+  if (!(eps > 0.0f) || !isfinite(eps)) return fail(FP8Q_EINVAL, "%s: eps must be finite and > 0", fn);
+  if (rows % 128 != 0) return fail(FP8Q_ESHAPE, "%s: rows (%lld) must be a multiple of 128", fn, (long long)rows);
+  if (cols % 64 != 0) return fail(FP8Q_ESHAPE, "%s: cols (%lld) must be a multiple of 64", fn, (long long)cols);
+  if (ldx < cols || ldq < rows || ld_s < rows / 128)
+    return fail(FP8Q_EINVAL, "%s: leading dimension smaller than the row", fn);
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scales, 4))
+    return fail(FP8Q_EALIGN, "%s: x and q must be 16-byte aligned, scales 4-byte", fn);
+  if ((ldx * esize(dt)) % 16 != 0 || ldq % 16 != 0)
+    return fail(FP8Q_EALIGN, "%s: ldx and ldq must keep rows 16-byte aligned", fn);
+  return launch_quantize_1x128_t(x, dt, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, S(stream));
+}
+
 int fp8q_quantize_128x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                           fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
                           int64_t ld_s, void* stream) {

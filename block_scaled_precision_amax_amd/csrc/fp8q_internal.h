@@ -138,6 +138,9 @@ int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const floa
 int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                           float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                           hipStream_t st);
+int launch_quantize_1x128_t(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                            float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                            hipStream_t st);
 int launch_quantize_128x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                             float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                             hipStream_t st);

@@ -19,6 +19,7 @@ namespace fp8q {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 static constexpr int kThreads = 256;
@@ -88,7 +89,7 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 #define FP8Q_KU_D 4
 #endif
 #ifndef FP8Q_G_D
-#define FP8Q_G_D 8
+#define FP8Q_G_D 32
 #endif
 
 template <int DT>
@@ -345,6 +346,79 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict
   }
 }
 
+// ---------------------------------------------------------------- 1x128 of the transpose
+// x [rows, cols] -> the codes of x^T [cols, rows], one scale per 128 rows of
+// a column of x (a 1x128 block of x^T: the layout the weight-gradient GEMM
+// takes for operands reduced over tokens).  One workgroup per 128x64 tile of
+// x, staged in LDS as fp32 with the column index XORed by 16*(row/32), which
+// keeps both the row-wise staging writes and the column-wise reads free of
+// bank conflicts.  Thread t owns column t/4 of the tile and rows
+// 32*(t%4) .. +32: the four lanes of a quad hold one column's 128 values,
+// reduce its amax with two shuffles and write its 128 codes as one
+// contiguous run of the transposed output.
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restrict__ x, int64_t ntc,
+                                                            int64_t ldx, float eps,
+                                                            uint8_t* __restrict__ q, int64_t ldq,
+                                                            float* __restrict__ scales, int64_t ld_s) {
+  __shared__ __attribute__((aligned(16))) float tile[128 * 64];
+  constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
+  constexpr int VE = 16 / esz;                 // elements per 16-byte vector
+  constexpr int VPR = 64 / VE;                 // vectors per tile row
+  constexpr int NVT = 128 * VPR / kThreads;    // vectors per thread
+  const int64_t rb = blockIdx.x / ntc, cb = blockIdx.x - rb * ntc;
+  const int64_t r0 = rb * 128, c0 = cb * 64;
+  const int tid = threadIdx.x;
+  const char* xb = (const char*)x;
+  u32x4 v[NVT];
+#pragma unroll
+  for (int i = 0; i < NVT; ++i) {
+    const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
+    v[i] = __builtin_nontemporal_load((const u32x4*)(xb + ((r0 + t) * ldx + c0 + c) * esz));
+  }
+#pragma unroll
+  for (int i = 0; i < NVT; ++i) {
+    const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
+    float* dst = tile + t * 64 + (c ^ (16 * (t >> 5)));
+    if constexpr (DT == FP8Q_F32) {
+      *(u32x4*)dst = v[i];
+    } else {
+      *(u32x4*)dst = u32x4{v[i].x << 16, v[i].x & 0xFFFF0000u, v[i].y << 16, v[i].y & 0xFFFF0000u};
+      *(u32x4*)(dst + 4) = u32x4{v[i].z << 16, v[i].z & 0xFFFF0000u, v[i].w << 16, v[i].w & 0xFFFF0000u};
+    }
+  }
+  __syncthreads();
+  const int f = tid >> 2, k = tid & 3;
+  const int fc = f ^ (16 * k);
+  float a[32];
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    a[j] = tile[(32 * k + j) * 64 + fc];
+    m = max(m, __float_as_uint(a[j]) & 0x7FFFFFFFu);
+  }
+  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
+  const int64_t col = c0 + f;
+  if (k == 0) scales[col * ld_s + rb] = s;
+  uint32_t w[8];
+  if (scale_ok(s)) {
+    // |x| <= amax, so x/s stays within the finite range
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = pack4<FMT>(sat<FMT>(div_rn(a[4 * i], s, r)), sat<FMT>(div_rn(a[4 * i + 1], s, r)),
+                        sat<FMT>(div_rn(a[4 * i + 2], s, r)), sat<FMT>(div_rn(a[4 * i + 3], s, r)));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = quant4_exact<FMT>(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3], s);
+  }
+  u32x4* dst = (u32x4*)(q + col * ldq + r0 + 32 * k);
+  __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, dst);
+  __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, dst + 1);
+}
+
 // ---------------------------------------------------------------- 128x128
 // One workgroup per 128x128 tile: the tile is read into registers once
 // (bf16: 8 rows x 16 B per thread; fp32: 16 rows x 16 B), its amax found
@@ -482,48 +556,80 @@ __device__ __forceinline__ float canon_nan(float f) {
   return f != f ? __uint_as_float(0x7FC00000u) : f;
 }
 
-// Work unit: (row, chunk of 1024*FP8Q_KU_D columns); each thread handles
-// FP8Q_KU_D groups of 4 codes, lanes on consecutive dwords (one dword load;
-// one 16-byte fp32 or 8-byte bf16 store each).
-template <int FMT, int GRAN, int ODT>
+// Work unit: (row, chunk of kThreads*8*FP8Q_KU_D columns); each thread
+// handles FP8Q_KU_D groups of 8 codes, lane l at codes 8l .. 8l+8 of the
+// group, so every load and store instruction of a wavefront covers one
+// contiguous run (512 bytes of codes, 1 KB of bf16).  V16: rows keep
+// 16-byte alignment (8-byte code loads, 16-byte bf16 stores); otherwise
+// dword loads and 8-byte stores.  Each workgroup walks a contiguous range
+// of units.  y = fl32(dec(q) * s), NaN made 0x7FC00000; bf16 output rounds
+// that to nearest even (the hardware conversion, which keeps subnormals and
+// maps the quiet NaN to 0x7FC0).
+template <int FMT, int GRAN, int ODT, bool V16>
 __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict__ q, int64_t rows,
                                                       int64_t cols, int64_t ldq,
                                                       const float* __restrict__ scales,
                                                       int64_t ld_s, void* __restrict__ y,
-                                                      int64_t ldy) {
-  constexpr int64_t CW = 1024 * FP8Q_KU_D;
-  const int64_t nchunk = (cols + CW - 1) / CW;
+                                                      int64_t ldy, int64_t per_wg) {
+  constexpr int64_t CW = kThreads * 8;
+  constexpr int64_t UW = CW * FP8Q_KU_D;
+  const int64_t nchunk = (cols + UW - 1) / UW;
   const int64_t units = rows * nchunk;
-  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+  int64_t u = (int64_t)blockIdx.x * per_wg;
+  const int64_t uend = u + per_wg < units ? u + per_wg : units;
+  for (; u < uend; ++u) {
     const int64_t r = u / nchunk, ch = u - r * nchunk;
 #pragma unroll
     for (int g = 0; g < FP8Q_KU_D; ++g) {
-      const int64_t c = ch * CW + g * 1024 + 4 * threadIdx.x;
+      const int64_t c = ch * UW + g * CW + 8 * threadIdx.x;
       if (c >= cols) break;
       float s;
       if constexpr (GRAN == FP8Q_GRAN_TENSOR) s = scales[0];
       else if constexpr (GRAN == FP8Q_GRAN_1x128) s = scales[r * ld_s + (c >> 7)];
       else s = scales[(r >> 7) * ld_s + (c >> 7)];
       const uint8_t* qp = q + r * ldq + c;
-      if (c + 4 <= cols) {
-        const uint32_t w = __builtin_nontemporal_load((const uint32_t*)qp);
-        const float2 lo = dec2<FMT>(w, false), hi = dec2<FMT>(w, true);
-        const float o0 = canon_nan(lo.x * s), o1 = canon_nan(lo.y * s);
-        const float o2 = canon_nan(hi.x * s), o3 = canon_nan(hi.y * s);
-        if constexpr (ODT == FP8Q_F32) {
-          u32x4 o = {__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
-          __builtin_nontemporal_store(o, (u32x4*)((float*)y + r * ldy + c));
+      if (c + 8 <= cols) {
+        u32x2 w;
+        if constexpr (V16) {
+          w = __builtin_nontemporal_load((const u32x2*)qp);
         } else {
-          u32x2 o;
-          o.x = f32_to_bf16(o0) | (f32_to_bf16(o1) << 16);
-          o.y = f32_to_bf16(o2) | (f32_to_bf16(o3) << 16);
-          __builtin_nontemporal_store(o, (u32x2*)((uint16_t*)y + r * ldy + c));
+          w.x = __builtin_nontemporal_load((const uint32_t*)qp);
+          w.y = __builtin_nontemporal_load((const uint32_t*)qp + 1);
+        }
+        float o[8];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const float2 lo = dec2<FMT>(w[k], false), hi = dec2<FMT>(w[k], true);
+          o[4 * k] = canon_nan(lo.x * s);
+          o[4 * k + 1] = canon_nan(lo.y * s);
+          o[4 * k + 2] = canon_nan(hi.x * s);
+          o[4 * k + 3] = canon_nan(hi.y * s);
+        }
+        if constexpr (ODT == FP8Q_F32) {
+          float* yp = (float*)y + r * ldy + c;
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const u32x4 v = {__float_as_uint(o[4 * k]), __float_as_uint(o[4 * k + 1]), __float_as_uint(o[4 * k + 2]),
+                             __float_as_uint(o[4 * k + 3])};
+            __builtin_nontemporal_store(v, (u32x4*)yp + k);
+          }
+        } else {
+          uint32_t b[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) b[k] = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o[2 * k], (__bf16)o[2 * k + 1]});
+          uint16_t* yp = (uint16_t*)y + r * ldy + c;
+          if constexpr (V16) {
+            __builtin_nontemporal_store(u32x4{b[0], b[1], b[2], b[3]}, (u32x4*)yp);
+          } else {
+            __builtin_nontemporal_store(u32x2{b[0], b[1]}, (u32x2*)yp);
+            __builtin_nontemporal_store(u32x2{b[2], b[3]}, (u32x2*)yp + 1);
+          }
         }
       } else {
         for (int64_t j = c; j < cols; ++j) {
           const float o = canon_nan(dec2<FMT>(q[r * ldq + j], false).x * s);
           if constexpr (ODT == FP8Q_F32) ((float*)y)[r * ldy + j] = o;
-          else ((uint16_t*)y)[r * ldy + j] = (uint16_t)f32_to_bf16(o);
+          else ((uint16_t*)y)[r * ldy + j] = __builtin_bit_cast(uint16_t, (__bf16)o);
         }
       }
     }
@@ -593,6 +699,25 @@ int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int
 }
 
 template <int DT, int FMT>
+static void launch_q1t(int64_t tiles, const void* x, int64_t ntc, int64_t ldx, float eps, uint8_t* q,
+                       int64_t ldq, float* scales, int64_t ld_s, hipStream_t st) {
+  hipLaunchKernelGGL((k_quant_1x128_t<DT, FMT>), dim3((unsigned)tiles), dim3(kThreads), 0, st, x, ntc, ldx, eps, q,
+                     ldq, scales, ld_s);
+}
+
+int launch_quantize_1x128_t(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
+                            float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
+                            hipStream_t st) {
+  const int64_t ntc = cols / 64, tiles = (rows / 128) * ntc;
+  if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "quantize_1x128_t: more than 2^31-1 tiles");
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_F32, FP8Q_E4M3FN>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (dt == FP8Q_F32) launch_q1t<FP8Q_F32, FP8Q_E5M2>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_BF16, FP8Q_E4M3FN>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
+  else launch_q1t<FP8Q_BF16, FP8Q_E5M2>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
+  return check_launch("quantize_1x128_t");
+}
+
+template <int DT, int FMT>
 static void launch_q128(int64_t tiles, const void* x, int64_t nkb, int64_t ldx, float eps, uint8_t* q,
                         int64_t ldq, float* scales, int64_t ld_s, hipStream_t st) {
   hipLaunchKernelGGL((k_quant_128x128<DT, FMT>), dim3((unsigned)tiles), dim3(kThreads), 0, st, x, nkb,
@@ -625,12 +750,19 @@ int launch_scaler_update(fp8q_scaler* s, float* amax, hipStream_t st) {
 template <int FMT, int GRAN, int ODT>
 static void launch_dq(const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const float* scales,
                       int64_t ld_s, void* y, int64_t ldy, hipStream_t st) {
-  const int64_t units = rows * ((cols + 1024 * FP8Q_KU_D - 1) / (1024 * FP8Q_KU_D));
-  int64_t grid = units;
-  const int64_t cap = (int64_t)device_cu_count() * FP8Q_G_D;
-  if (grid > cap) grid = cap;
-  hipLaunchKernelGGL((k_dequant<FMT, GRAN, ODT>), dim3((unsigned)grid), dim3(kThreads), 0, st, q, rows,
-                     cols, ldq, scales, ld_s, y, ldy);
+  const int64_t uw = (int64_t)kThreads * 8 * FP8Q_KU_D;
+  const int64_t units = rows * ((cols + uw - 1) / uw);
+  const int grid = chunk_grid(units, FP8Q_G_D);
+  const int64_t per_wg = (units + grid - 1) / grid;
+  // 16-byte rows: q and y are 16-byte aligned, so every row is when the
+  // leading dimensions keep 16 bytes (a single row always does)
+  const bool v16 = rows == 1 || (ldq % 16 == 0 && (ldy * (ODT == FP8Q_F32 ? 4 : 2)) % 16 == 0);
+  if (v16)
+    hipLaunchKernelGGL((k_dequant<FMT, GRAN, ODT, true>), dim3(grid), dim3(kThreads), 0, st, q, rows, cols, ldq,
+                       scales, ld_s, y, ldy, per_wg);
+  else
+    hipLaunchKernelGGL((k_dequant<FMT, GRAN, ODT, false>), dim3(grid), dim3(kThreads), 0, st, q, rows, cols, ldq,
+                       scales, ld_s, y, ldy, per_wg);
 }
 
 template <int FMT, int GRAN>

@@ -113,6 +113,23 @@ int fp8q_quantize_1x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols
                         fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
                         int64_t ld_s, void* stream);
 
+/* Fine-grained 1x128 quantization of the transpose: the operands of the
+ * weight-gradient GEMM are reduced over tokens, so activations and output
+ * gradients stored [tokens, features] are needed as [features, tokens]
+ * codes with one scale per 128 tokens ([H] fine-grained scaling along the
+ * reduced dimension; [A] 6.3 E5M2 gradients).  Equal to fp8q_quantize_1x128
+ * of x^T, without materializing x^T:
+ *   for column c of x and row block rb:
+ *   s = scale(amax(x[128rb : 128rb+128, c]), eps), q[c, r] = enc(fl32(x[r, c]/s)).
+ * x: rows x cols, element (r,c) at x[r*ldx + c]; rows % 128 == 0,
+ *   cols % 64 == 0; ldx >= cols; x and ldx*sizeof(dt) 16-B aligned.
+ * q: codes of x^T at q[c*ldq + r]; ldq >= rows, q and ldq 16-B aligned.
+ * scales: fp32 at scales[c*ld_s + rb], ld_s >= rows/128.
+ * eps: lower clamp of amax; must be > 0. */
+int fp8q_quantize_1x128_t(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
+                          fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
+                          int64_t ld_s, void* stream);
+
 /* Fine-grained 128x128 quantization of weights ([H] per_block(x, 128,
  * 128)).  As fp8q_quantize_1x128 with one scale per 128x128 tile:
  * scales[rb*ld_s + kb] for rows 128rb.. and columns 128kb..;

@@ -97,6 +97,26 @@ def test_block_quantize_validation(fq, fn, br):
         assert call(rows=0)[0] == fq.EINVAL
 
 
+def test_transposed_quantize_validation(fq):
+    ok = dict(x=FAKE, dt=1, rows=256, cols=128, ldx=128, f=0, eps=1e-12, q=FAKE, ldq=256, s=FAKE, ld_s=2)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return _rc(fq, "fp8q_quantize_1x128_t", a["x"], a["dt"], a["rows"], a["cols"], a["ldx"], a["f"],
+                   a["eps"], a["q"], a["ldq"], a["s"], a["ld_s"], None)
+
+    assert call(q=None)[0] == fq.EINVAL
+    assert call(f=2)[0] == fq.EINVAL
+    rc, msg = call(rows=200, ldq=256)
+    assert rc == fq.ESHAPE and "multiple of 128" in msg
+    rc, msg = call(cols=96, ldx=128)
+    assert rc == fq.ESHAPE and "multiple of 64" in msg
+    assert call(ldq=128)[0] == fq.EINVAL
+    assert call(ld_s=1)[0] == fq.EINVAL
+    assert call(ldx=132)[0] == fq.EALIGN
+    assert call(ldq=264)[0] == fq.EALIGN
+
+
 def test_scaler_validation(fq):
     assert _rc(fq, "fp8q_delayed_scaler_init", None, 16, 448.0, 1e-12, 1.0, None)[0] == fq.EINVAL
     assert _rc(fq, "fp8q_delayed_scaler_init", FAKE, 0, 448.0, 1e-12, 1.0, None)[0] == fq.EINVAL

@@ -318,6 +318,64 @@ def test_full_size_weight_128x128_fp32(fq, orc, gpu):
     assert np.array_equal(f32bits(s), f32bits(ws))
 
 
+# ------------------------------------------------------------------ 1x128 of the transpose
+def run_block_t(fq, x_dev, rows, cols, ldx, fmt, pad_q=0, pad_s=0):
+    """fp8q_quantize_1x128_t of the rows x cols view of x_dev: codes [cols, rows]."""
+    ldq, ld_s = rows + pad_q, rows // 128 + pad_s
+    q = torch.full((cols, ldq), 0xAA, dtype=torch.uint8, device=x_dev.device)
+    s = torch.full((cols, ld_s), -7.0, dtype=torch.float32, device=x_dev.device)
+    fq.fp8q_quantize_1x128_t(x_dev, rows, cols, ldx, fmt, EPS, q, ldq, s, ld_s)
+    torch.cuda.synchronize()
+    qn, sn = q.cpu().numpy(), s.cpu().numpy()
+    assert np.all(qn[:, rows:] == 0xAA), "wrote past the row"
+    assert np.all(sn[:, rows // 128:] == -7.0), "wrote past the scale row"
+    return qn[:, :rows], sn[:, :rows // 128]
+
+
+def oracle_t(orc, x_np, fmt):
+    """The definition: 1x128 quantization of the transpose."""
+    return orc.quantize_1x128(np.ascontiguousarray(x_np.T), fmt, EPS)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("rows,cols,ldx,pad_q", [(128, 64, 64, 0), (256, 192, 200, 32), (384, 128, 136, 16),
+                                                 (128, 1024, 1024, 0)])
+def test_quantize_1x128_t(fq, orc, gpu, dt, fmt, rows, cols, ldx, pad_q):
+    rng = np.random.default_rng(rows + cols + fmt)
+    x = (rng.standard_normal((rows, ldx)) * np.exp(rng.standard_normal((1, ldx)) * 3)).astype(np.float32)
+    xd = torch.from_numpy(x).to(dt).to(gpu)
+    xv = W.to_numpy_input(xd.cpu())[:, :cols]
+    q, s = run_block_t(fq, xd, rows, cols, ldx, fmt, pad_q=pad_q, pad_s=1)
+    wq, ws = oracle_t(orc, xv, fmt)
+    assert_codes_equal(q, wq)
+    assert np.array_equal(f32bits(s), f32bits(ws))
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_1x128_t_special_values(fq, orc, gpu, dt, fmt):
+    """Every special block (zeros, NaN, Inf, denormals, below eps, huge,
+    rounding midpoints) as 128-row column segments."""
+    x = np.ascontiguousarray(special_blocks_fp32(np.random.default_rng(11), 64).T)  # 1024 x 64
+    xd = torch.from_numpy(x).to(dt).to(gpu)
+    xv = W.to_numpy_input(xd.cpu())
+    q, s = run_block_t(fq, xd, 1024, 64, 64, fmt)
+    wq, ws = oracle_t(orc, xv, fmt)
+    assert_codes_equal(q, wq)
+    assert np.array_equal(f32bits(s), f32bits(ws))
+
+
+def test_quantize_1x128_t_full_wgrad_operand(fq, orc, gpu):
+    """The weight-gradient operand: bf16 activations [16384 tokens, 4096]
+    N(0,1), quantized to E4M3FN codes [4096, 16384] with scales per 128 tokens."""
+    x = W.normal((16384, 4096), seed=52, device=gpu, dtype=torch.bfloat16)
+    q, s = run_block_t(fq, x, 16384, 4096, 4096, E4)
+    wq, ws = oracle_t(orc, W.to_numpy_input(x.cpu()), E4)
+    assert_codes_equal(q, wq)
+    assert np.array_equal(f32bits(s), f32bits(ws))
+
+
 # ------------------------------------------------------------------ dequantize
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("gran", [0, 1, 2])
@@ -338,6 +396,29 @@ def test_dequantize(fq, orc, gpu, fmt, gran, out):
     # bit patterns (NaN results are the canonical quiet NaN on both sides)
     assert np.array_equal(got.view(np.uint32 if out == torch.float32 else np.uint16),
                           want.view(np.uint32 if out == torch.float32 else np.uint16))
+
+
+@pytest.mark.parametrize("gran,rows,cols,ld", [(0, 100, 1000, 1004), (1, 100, 384, 388), (2, 300, 384, 388),
+                                                 (0, 3, 4096, 4100), (1, 129, 512, 528)])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_dequantize_strided(fq, orc, gpu, gran, rows, cols, ld, out):
+    """Leading dimensions that are not 16-byte row strides (the dword path) or
+    are (ld 528), rows whose length is not a multiple of 16 codes, and a
+    subnormal scale."""
+    q = W.fp8_codes((rows, ld), E4, seed=rows + cols)
+    rng = np.random.default_rng(ld)
+    shape = {0: (1, 1), 1: (rows, cols // 128), 2: ((rows + 127) // 128, cols // 128)}[gran]
+    s = np.exp(rng.standard_normal(shape) * 5).astype(np.float32)
+    s.reshape(-1)[-1] = np.float32(3e-41)
+    y = torch.full((rows, ld), 7.0, dtype=out, device=gpu)
+    fq.fp8q_dequantize(q.to(gpu), E4, rows, cols, ld, torch.from_numpy(s).to(gpu), gran, shape[1], y, ld)
+    torch.cuda.synchronize()
+    want = orc.dequantize(np.ascontiguousarray(q.numpy()[:, :cols]), E4, s, gran, out_bf16=out == torch.bfloat16)
+    bits = np.uint32 if out == torch.float32 else np.uint16
+    got = y.cpu().view(torch.int32 if out == torch.float32 else torch.int16).numpy().view(bits)
+    assert np.array_equal(got[:, :cols], want.view(bits))
+    pad = np.float32(7.0).view(np.uint32) if out == torch.float32 else np.uint16(0x40E0)
+    assert np.all(got[:, cols:] == pad), "dequantize wrote past the row"
 
 
 def test_dequantize_flat_ragged(fq, orc, gpu):
