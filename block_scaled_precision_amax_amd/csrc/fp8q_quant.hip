@@ -349,74 +349,98 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict
 // ---------------------------------------------------------------- 1x128 of the transpose
 // x [rows, cols] -> the codes of x^T [cols, rows], one scale per 128 rows of
 // a column of x (a 1x128 block of x^T: the layout the weight-gradient GEMM
-// takes for operands reduced over tokens).  One workgroup per 128x64 tile of
-// x, staged in LDS as fp32 with the column index XORed by 16*(row/32), which
-// keeps both the row-wise staging writes and the column-wise reads free of
-// bank conflicts.  Thread t owns column t/4 of the tile and rows
-// 32*(t%4) .. +32: the four lanes of a quad hold one column's 128 values,
-// reduce its amax with two shuffles and write its 128 codes as one
-// contiguous run of the transposed output.
+// takes for operands reduced over tokens).  A workgroup takes a 64-column
+// slab of x and walks FP8Q_RT consecutive 128-row blocks of it, loading the
+// next block while it encodes the current one.  Each 128x64 tile is staged
+// in LDS in its input type with the column index XORed by
+// 16*((row/16) mod 4), which keeps the row-wise staging writes and the
+// column-wise reads free of bank conflicts.  The four lanes of a quad hold
+// one column's 128 values, reduce its amax with two shuffles and write its
+// 128 codes as one contiguous run of the transposed output.
+#ifndef FP8Q_RT
+#define FP8Q_RT 16  // row blocks per workgroup in the transposed quantizer (measured)
+#endif
 template <int DT, int FMT>
 __global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restrict__ x, int64_t ntc,
-                                                            int64_t ldx, float eps,
+                                                            int64_t nrb, int64_t ldx, float eps,
                                                             uint8_t* __restrict__ q, int64_t ldq,
                                                             float* __restrict__ scales, int64_t ld_s) {
-  __shared__ __attribute__((aligned(16))) float tile[128 * 64];
+  // bf16 stays bf16 in LDS (16 KB per workgroup)
+  __shared__ __attribute__((aligned(16))) uint32_t tile_raw[DT == FP8Q_F32 ? 128 * 64 : 128 * 32];
+  float* tile = (float*)tile_raw;
+  uint16_t* tile16 = (uint16_t*)tile_raw;
   constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
   constexpr int VE = 16 / esz;                 // elements per 16-byte vector
   constexpr int VPR = 64 / VE;                 // vectors per tile row
   constexpr int NVT = 128 * VPR / kThreads;    // vectors per thread
-  const int64_t rb = blockIdx.x / ntc, cb = blockIdx.x - rb * ntc;
-  const int64_t r0 = rb * 128, c0 = cb * 64;
+  // workgroup -> (group of FP8Q_RT row blocks, 64-column slab)
+  const int64_t cb = blockIdx.x % ntc, rg = blockIdx.x / ntc;
+  const int64_t c0 = cb * 64;
+  const int64_t rb_begin = rg * FP8Q_RT;
+  const int64_t rb_end = rb_begin + FP8Q_RT < nrb ? rb_begin + FP8Q_RT : nrb;
   const int tid = threadIdx.x;
   const char* xb = (const char*)x;
-  u32x4 v[NVT];
+  auto load = [&](int64_t rb, u32x4* v) {
 #pragma unroll
-  for (int i = 0; i < NVT; ++i) {
-    const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
-    v[i] = __builtin_nontemporal_load((const u32x4*)(xb + ((r0 + t) * ldx + c0 + c) * esz));
-  }
-#pragma unroll
-  for (int i = 0; i < NVT; ++i) {
-    const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
-    float* dst = tile + t * 64 + (c ^ (16 * (t >> 5)));
-    if constexpr (DT == FP8Q_F32) {
-      *(u32x4*)dst = v[i];
-    } else {
-      *(u32x4*)dst = u32x4{v[i].x << 16, v[i].x & 0xFFFF0000u, v[i].y << 16, v[i].y & 0xFFFF0000u};
-      *(u32x4*)(dst + 4) = u32x4{v[i].z << 16, v[i].z & 0xFFFF0000u, v[i].w << 16, v[i].w & 0xFFFF0000u};
+    for (int i = 0; i < NVT; ++i) {
+      const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
+      v[i] = __builtin_nontemporal_load((const u32x4*)(xb + ((rb * 128 + t) * ldx + c0 + c) * esz));
     }
-  }
-  __syncthreads();
+  };
+  // thread (f, k): column f, rows 16k .. 16k+16 and 64+16k .. 64+16k+16,
+  // so that each of its two 16-byte code stores lands next to those of the
+  // other three lanes of the quad (64 contiguous bytes per store)
+  auto swz = [](int t) { return 16 * ((t >> 4) & 3); };
   const int f = tid >> 2, k = tid & 3;
   const int fc = f ^ (16 * k);
-  float a[32];
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    a[j] = tile[(32 * k + j) * 64 + fc];
-    m = max(m, __float_as_uint(a[j]) & 0x7FFFFFFFu);
-  }
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-  const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
   const int64_t col = c0 + f;
-  if (k == 0) scales[col * ld_s + rb] = s;
-  uint32_t w[8];
-  if (scale_ok(s)) {
-    // |x| <= amax, so x/s stays within the finite range
-    const float r = 1.0f / s;
+  u32x4 v[NVT], vn[NVT];
+  load(rb_begin, v);
+  for (int64_t rb = rb_begin; rb < rb_end; ++rb) {
+    if (rb + 1 < rb_end) load(rb + 1, vn);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      w[i] = pack4<FMT>(sat<FMT>(div_rn(a[4 * i], s, r)), sat<FMT>(div_rn(a[4 * i + 1], s, r)),
-                        sat<FMT>(div_rn(a[4 * i + 2], s, r)), sat<FMT>(div_rn(a[4 * i + 3], s, r)));
-  } else {
+    for (int i = 0; i < NVT; ++i) {
+      const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
+      if constexpr (DT == FP8Q_F32)
+        *(u32x4*)(tile + t * 64 + (c ^ swz(t))) = v[i];
+      else
+        *(u32x4*)(tile16 + t * 64 + (c ^ swz(t))) = v[i];
+    }
+    __syncthreads();
+    float a[32];
+    uint32_t m = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = quant4_exact<FMT>(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3], s);
+    for (int j = 0; j < 32; ++j) {
+      const int t = 16 * k + (j & 15) + 64 * (j >> 4);  // swz(t) == 16k
+      if constexpr (DT == FP8Q_F32)
+        a[j] = tile[t * 64 + fc];
+      else
+        a[j] = __uint_as_float((uint32_t)tile16[t * 64 + fc] << 16);
+      m = max(m, __float_as_uint(a[j]) & 0x7FFFFFFFu);
+    }
+    __syncthreads();  // the tile is rewritten by the next row block
+    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+    const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
+    if (k == 0) scales[col * ld_s + rb] = s;
+    uint32_t w[8];
+    if (scale_ok(s)) {
+      // |x| <= amax, so x/s stays within the finite range
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        w[i] = pack4<FMT>(sat<FMT>(div_rn(a[4 * i], s, r)), sat<FMT>(div_rn(a[4 * i + 1], s, r)),
+                          sat<FMT>(div_rn(a[4 * i + 2], s, r)), sat<FMT>(div_rn(a[4 * i + 3], s, r)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w[i] = quant4_exact<FMT>(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3], s);
+    }
+    uint8_t* qrow = q + col * ldq + rb * 128 + 16 * k;
+    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)qrow);
+    __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, (u32x4*)(qrow + 64));
+#pragma unroll
+    for (int i = 0; i < NVT; ++i) v[i] = vn[i];
   }
-  u32x4* dst = (u32x4*)(q + col * ldq + r0 + 32 * k);
-  __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, dst);
-  __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, dst + 1);
 }
 
 // ---------------------------------------------------------------- 128x128
@@ -699,21 +723,22 @@ int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int
 }
 
 template <int DT, int FMT>
-static void launch_q1t(int64_t tiles, const void* x, int64_t ntc, int64_t ldx, float eps, uint8_t* q,
+static void launch_q1t(int64_t wgs, const void* x, int64_t ntc, int64_t nrb, int64_t ldx, float eps, uint8_t* q,
                        int64_t ldq, float* scales, int64_t ld_s, hipStream_t st) {
-  hipLaunchKernelGGL((k_quant_1x128_t<DT, FMT>), dim3((unsigned)tiles), dim3(kThreads), 0, st, x, ntc, ldx, eps, q,
-                     ldq, scales, ld_s);
+  hipLaunchKernelGGL((k_quant_1x128_t<DT, FMT>), dim3((unsigned)wgs), dim3(kThreads), 0, st, x, ntc, nrb, ldx, eps,
+                     q, ldq, scales, ld_s);
 }
 
 int launch_quantize_1x128_t(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                             float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                             hipStream_t st) {
-  const int64_t ntc = cols / 64, tiles = (rows / 128) * ntc;
-  if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "quantize_1x128_t: more than 2^31-1 tiles");
-  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_F32, FP8Q_E4M3FN>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
-  else if (dt == FP8Q_F32) launch_q1t<FP8Q_F32, FP8Q_E5M2>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
-  else if (fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_BF16, FP8Q_E4M3FN>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
-  else launch_q1t<FP8Q_BF16, FP8Q_E5M2>(tiles, x, ntc, ldx, eps, q, ldq, scales, ld_s, st);
+  const int64_t ntc = cols / 64, nrb = rows / 128;
+  const int64_t wgs = ((nrb + FP8Q_RT - 1) / FP8Q_RT) * ntc;
+  if (wgs > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "quantize_1x128_t: more than 2^31-1 workgroups");
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_F32, FP8Q_E4M3FN>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (dt == FP8Q_F32) launch_q1t<FP8Q_F32, FP8Q_E5M2>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_BF16, FP8Q_E4M3FN>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  else launch_q1t<FP8Q_BF16, FP8Q_E5M2>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
   return check_launch("quantize_1x128_t");
 }
 
