@@ -58,6 +58,10 @@ def lib() -> ctypes.CDLL:
             "orc_encode_array": (None, [vp, i64, i32, vp]),
             "orc_encode_bits_range": (None, [u32, i64, i32, vp]),
             "orc_amax": (f32, [vp, i32, i64]),
+            "orc_quantize_mx": (None, [vp, i32, i64, i64, i64, i32, vp, i64, vp, i64]),
+            "orc_dequantize_mx": (None, [vp, i32, i64, i64, i64, vp, i64, vp, i64]),
+            "orc_gemm_mx": (None, [vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, i64, i64, i64, vp, i64, vp,
+                                   vp]),
             "orc_scale": (f32, [f32, f32, f32, f32]),
             "orc_quantize_value": (u32, [f32, f32, i32]),
             "orc_quantize_tensor": (None, [vp, i32, i64, i32, f32, vp]),
@@ -221,4 +225,50 @@ def gemm_blockscaled(A: np.ndarray, fa: int, sA: np.ndarray, B: np.ndarray, fb: 
     lib().orc_gemm_blockscaled(_ptr(A), fa, K, _ptr(sA), sA.shape[1], 1, _ptr(B), fb, K, _ptr(sB), gb,
                                sB.shape[1], 1, M, N, K, None if rp is None else _ptr(rp),
                                0 if rp is None else nr, _ptr(C), _ptr(D))
+    return C, D
+
+
+# ---------------------------------------------------------------- MX (microscaling) FP8
+def quantize_mx(x: np.ndarray, fmt: int):
+    """32-element blocks along rows with power-of-two E8M0 scales (OCP MX v1.0, 6.3).
+    Returns (codes [rows, cols], scale bytes [rows, cols/32])."""
+    x = np.ascontiguousarray(x)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    rows, cols = x.shape
+    assert cols % 32 == 0
+    q = np.empty((rows, cols), dtype=np.uint8)
+    s = np.empty((rows, cols // 32), dtype=np.uint8)
+    lib().orc_quantize_mx(_ptr(x), _dtype_code(x), rows, cols, cols, fmt, _ptr(q), cols, _ptr(s), cols // 32)
+    return q, s
+
+
+def dequantize_mx(q: np.ndarray, fmt: int, scales: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    rows, cols = q.shape
+    y = np.empty((rows, cols), dtype=np.float32)
+    lib().orc_dequantize_mx(_ptr(q), fmt, rows, cols, cols, _ptr(scales), scales.shape[1], _ptr(y), cols)
+    return y
+
+
+def gemm_mx(A: np.ndarray, fa: int, sA: np.ndarray, B: np.ndarray, fb: int, sB: np.ndarray,
+            rows: np.ndarray | None = None):
+    """C, D of the MX GEMM: A [M,K], B [N,K] codes, E8M0 scales sA [M,K/32], sB [N,K/32]."""
+    A = np.ascontiguousarray(A, dtype=np.uint8)
+    B = np.ascontiguousarray(B, dtype=np.uint8)
+    sA = np.ascontiguousarray(sA, dtype=np.uint8)
+    sB = np.ascontiguousarray(sB, dtype=np.uint8)
+    M, K = A.shape
+    N, K2 = B.shape
+    assert K == K2 and K % 32 == 0
+    if rows is None:
+        nr, rp = M, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        nr, rp = rows.size, rows
+    C = np.empty((nr, N), dtype=np.float64)
+    D = np.empty((nr, N), dtype=np.float64)
+    lib().orc_gemm_mx(_ptr(A), fa, K, _ptr(sA), sA.shape[1], _ptr(B), fb, K, _ptr(sB), sB.shape[1], M, N, K,
+                      None if rp is None else _ptr(rp), 0 if rp is None else nr, _ptr(C), _ptr(D))
     return C, D

@@ -26,6 +26,11 @@
  * round-to-nearest-even; overflow saturates to +-MAX for both formats;
  * signed zero is kept; a NaN input encodes as 0x7F; NaN propagates through
  * amax; scales are dequant scales s = max(amax, eps)*margin / MAX.
+ *
+ * MX (microscaling) FP8, which [H] names as the next, hardware-native step
+ * of fine-grained scaling without giving its algorithm, follows the public
+ * OCP Microscaling Formats (MX) specification v1.0, section 6.3; its
+ * readings are listed beside orc_quantize_mx below.
  */
 #include <math.h>
 #include <stdint.h>
@@ -335,6 +340,121 @@ void orc_gemm_blockscaled(const uint8_t* A, int fa, int64_t lda, const float* sA
         double coef = sa * sb; /* exact */
         c += coef * ldexp((double)p, -32);
         d += fabs(coef) * ldexp((double)pabs, -32);
+      }
+      if (special) c = NAN;
+      C[ri * N + n] = c;
+      D[ri * N + n] = d;
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* MX (microscaling) FP8.  The handbook names hardware-native block     */
+/* scaling with 32-element blocks and power-of-two (E8M0) shared scales */
+/* as the next step after 1x128 / 128x128 scaling; the pages give no    */
+/* algorithm, so this follows the public OCP Microscaling Formats (MX)  */
+/* specification v1.0 (section 6.3, conversion of a vector to MX):      */
+/*   e = floor(log2(max_i |V_i|)) - emax_elem,  X = 2^e,                */
+/*   P_i = quantize_to_element_format(V_i / X)  (RNE, clamped to the    */
+/*         largest normal),                                             */
+/* emax_elem = exponent of the element format's largest normal: 8 for   */
+/* E4M3 (448 = 1.75 * 2^8), 15 for E5M2 (57344 = 1.75 * 2^15).  X is    */
+/* stored as the E8M0 byte e + 127 (0xFF = NaN).  Readings where the    */
+/* specification leaves room: max |V| == 0 gives e = -127 (every code   */
+/* +-0); a NaN or an Inf in the block gives the NaN scale 0xFF and NaN  */
+/* codes 0x7F; e is clamped to [-127, 127].  Blocks are 32 consecutive  */
+/* elements of a row.                                                   */
+/* ------------------------------------------------------------------ */
+static int emax_elem(int fmt) { return fmt == ORC_E4M3FN ? 8 : 15; }
+
+void orc_quantize_mx(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                     int64_t ldq, uint8_t* scales, int64_t ld_s) {
+  int64_t nb = cols / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      double amax = 0.0;
+      int special = 0;
+      for (int64_t c = 32 * b; c < 32 * b + 32; ++c) {
+        float v = load_elem(x, dt, r * ldx + c);
+        if (isnan(v) || isinf(v)) special = 1;
+        else if (fabs((double)v) > amax) amax = fabs((double)v);
+      }
+      if (special) {
+        scales[r * ld_s + b] = 0xFF;
+        for (int64_t c = 32 * b; c < 32 * b + 32; ++c) q[r * ldq + c] = 0x7F;
+        continue;
+      }
+      int e = -127;
+      if (amax > 0.0) {
+        int E;
+        (void)frexp(amax, &E); /* amax = f * 2^E, f in [0.5, 1): floor(log2 amax) = E - 1 */
+        e = (E - 1) - emax_elem(fmt);
+      }
+      if (e < -127) e = -127;
+      if (e > 127) e = 127;
+      scales[r * ld_s + b] = (uint8_t)(e + 127);
+      for (int64_t c = 32 * b; c < 32 * b + 32; ++c) {
+        /* V / 2^e is exact in double; as a float it is exact whenever it
+           is at least the smallest FP8 subnormal, and anything below
+           half of that encodes as +-0 however it is rounded */
+        float y = (float)ldexp((double)load_elem(x, dt, r * ldx + c), -e);
+        q[r * ldq + c] = (uint8_t)orc_encode(y, fmt);
+      }
+    }
+}
+
+/* x^ = fl32(dec(q) * 2^(s - 127)); scale byte 0xFF makes NaN. */
+void orc_dequantize_mx(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
+                       const uint8_t* scales, int64_t ld_s, float* y, int64_t ldy) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c) {
+      uint8_t sb = scales[r * ld_s + c / 32];
+      double v = sb == 0xFF ? NAN : ldexp(orc_decode(q[r * ldq + c], fmt), (int)sb - 127);
+      float f = (float)v;
+      y[r * ldy + c] = isnan(f) ? canonical_nan() : f;
+    }
+}
+
+/* MX GEMM: C[m,n] = sum_kb 2^(ea + eb) * sum_{k in 32-block kb} dec(A[m,k]) dec(B[n,k]),
+   A [M,K] and B [N,K] K-contiguous, E8M0 scales sA[m*ld_sa + kb], sB[n*ld_sb + kb].
+   Block sums exact in __int128 (codes times 2^16 are integers), outer sum fp64.
+   D = sum_kb 2^(ea+eb) sum_k |dec(a) dec(b)|; a NaN or Inf code or a NaN scale
+   in a dot product makes C NaN there. */
+void orc_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
+                 int fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, int64_t M, int64_t N, int64_t K,
+                 const int64_t* rows, int64_t nrows, double* C, double* D) {
+  int64_t ta[256], tb[256];
+  unsigned char oka[256], okb[256];
+  int_table(fa, ta, oka);
+  int_table(fb, tb, okb);
+  int64_t nkb = K / 32;
+  int64_t nr = rows ? nrows : M;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t ri = 0; ri < nr; ++ri) {
+    int64_t m = rows ? rows[ri] : ri;
+    const uint8_t* arow = A + m * lda;
+    for (int64_t n = 0; n < N; ++n) {
+      const uint8_t* brow = B + n * ldb;
+      double c = 0.0, d = 0.0;
+      int special = 0;
+      for (int64_t kb = 0; kb < nkb; ++kb) {
+        uint8_t ea = sA[m * ld_sa + kb], eb = sB[n * ld_sb + kb];
+        if (ea == 0xFF || eb == 0xFF) special = 1;
+        __int128 p = 0, pabs = 0;
+        for (int64_t k = kb * 32; k < kb * 32 + 32; ++k) {
+          if (!oka[arow[k]] || !okb[brow[k]]) {
+            special = 1;
+            continue;
+          }
+          __int128 t = (__int128)ta[arow[k]] * (__int128)tb[brow[k]];
+          p += t;
+          pabs += t < 0 ? -t : t;
+        }
+        int sh = (int)ea + (int)eb - 254 - 32;
+        c += ldexp((double)p, sh);
+        d += ldexp((double)pabs, sh);
       }
       if (special) c = NAN;
       C[ri * N + n] = c;

@@ -452,3 +452,154 @@ def test_rel_err_matches_numpy_norm(orc):
     y = x + rng.standard_normal((17, 33)).astype(np.float32) * 0.01
     want = np.linalg.norm(y.astype(np.float64) - x.astype(np.float64)) / np.linalg.norm(x.astype(np.float64))
     assert abs(orc.rel_err(y, x) - want) < 1e-14
+
+
+# ------------------------------------------------------------------ MX (microscaling) FP8
+# The MX conversion of the OCP MX v1.0 specification (section 6.3): blocks of
+# 32 elements share X = 2^(floor(log2 max|V|) - emax_elem), stored as the
+# E8M0 byte e + 127; elements are RNE-cast with clamping to the largest normal.
+EMAX = {E4: 8, E5: 15}
+
+
+def _mx_block(vals):
+    return np.array([vals + [0.0] * (32 - len(vals))], dtype=np.float32)
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_mx_scale_byte_closed_forms(orc, fmt):
+    """Scale byte = floor(log2 amax) - emax + 127 at and between powers of two,
+    and the block maximum lands in [2^emax, 2^(emax+1)) after scaling."""
+    for amax, fl in [(1.0, 0), (1.5, 0), (1.9999, 0), (2.0, 1), (3.0, 1), (448.0, 8), (0.75, -1),
+                     (2.0 ** -20, -20), (2.0 ** 100 * 1.3, 100)]:
+        _, s = orc.quantize_mx(_mx_block([amax, -amax / 3]), fmt)
+        assert int(s[0, 0]) == fl - EMAX[fmt] + 127, (amax, s)
+    # the largest representable block maximum with scale 2^0 is exactly the format's max
+    q, s = orc.quantize_mx(_mx_block([MAXF[fmt]]), fmt)
+    if fmt == E4:
+        assert int(s[0, 0]) == 127 and int(q[0, 0]) == MAXCODE[fmt]
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_mx_elements_match_torch_cast(orc, fmt):
+    """Element codes equal torch's float8 cast of V / X (exact power-of-two
+    division) wherever that cast does not overflow; values between the
+    format's max and the next binade clamp to the max code."""
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((64, 256)) * np.exp(rng.standard_normal((64, 1)) * 4)).astype(np.float32)
+    q, s = orc.quantize_mx(x, fmt)
+    X = np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    y = (x.astype(np.float64) / X).astype(np.float32)
+    over = np.abs(y) > MAXF[fmt]
+    tq = torch.from_numpy(np.where(over, 0, y)).to(TORCH_FP8[fmt]).view(torch.uint8).numpy()
+    assert np.array_equal(q[~over], tq[~over])
+    assert np.all((q[over] & 0x7F) == MAXCODE[fmt]) and np.array_equal(q[over] >> 7, (y[over] < 0).astype(np.uint8))
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_mx_power_of_two_equivariance(orc, fmt):
+    """Scaling a block by 2^k leaves every code unchanged and adds k to the scale byte."""
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((8, 128)).astype(np.float32)
+    q0, s0 = orc.quantize_mx(x, fmt)
+    for k in (-30, -7, -1, 1, 5, 40):
+        q, s = orc.quantize_mx(np.ldexp(x, k).astype(np.float32), fmt)
+        assert np.array_equal(q, q0) and np.array_equal(s.astype(np.int64), s0.astype(np.int64) + k)
+
+
+def test_mx_special_blocks(orc):
+    """Zero block: scale byte 0 (2^-127) and zero codes, signs kept; a NaN or an
+    Inf anywhere: NaN scale 0xFF and NaN codes."""
+    x = np.zeros((4, 32), np.float32)
+    x[0, 3] = -0.0
+    x[1, 5] = np.nan
+    x[2, 7] = -np.inf
+    x[3, :] = 1.0
+    q, s = orc.quantize_mx(x, E4)
+    assert int(s[0, 0]) == 0 and np.all(q[0, :3] == 0) and q[0, 3] == 0x80
+    assert int(s[1, 0]) == 0xFF and np.all(q[1] == 0x7F)
+    assert int(s[2, 0]) == 0xFF and np.all(q[2] == 0x7F)
+    assert int(s[3, 0]) == 119
+    y = orc.dequantize_mx(q, E4, s)
+    assert np.all(np.isnan(y[1])) and np.all(y[3] == 1.0) and np.signbit(y[0, 3])
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_mx_dequantize_closed_form(orc, fmt):
+    """Every finite code times 2^(byte - 127), for a spread of scale bytes,
+    against Python's exact ldexp of the decoded value."""
+    codes = np.array([c for c in range(256) if math.isfinite(orc.decode(c, fmt))], np.uint8)
+    n = (codes.size // 32) * 32
+    codes = codes[:n].reshape(-1, 32)
+    for b in (1, 60, 127, 128, 200, 254):
+        s = np.full((codes.shape[0], 1), b, np.uint8)
+        y = orc.dequantize_mx(codes, fmt, s)
+        want = np.array([[np.float32(math.ldexp(orc.decode(int(c), fmt), b - 127)) for c in row] for row in codes])
+        assert np.array_equal(y.view(np.uint32), want.astype(np.float32).view(np.uint32)), b
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_mx_round_trip_error_bound(orc, fmt):
+    """|dequant(quant(x)) - x| <= max(|x| * 2^-(M+1), X * 2^(emin - M - 1)) for
+    unclamped values (half an ulp, or half the subnormal quantum)."""
+    M = 3 if fmt == E4 else 2
+    emin = -6 if fmt == E4 else -14
+    rng = np.random.default_rng(23)
+    x = (rng.standard_normal((32, 256)) * np.exp(rng.standard_normal((32, 8)).repeat(32, axis=1) * 3)).astype(np.float32)
+    q, s = orc.quantize_mx(x, fmt)
+    y = orc.dequantize_mx(q, fmt, s).astype(np.float64)
+    X = np.ldexp(1.0, s.astype(np.int64) - 127).repeat(32, axis=1)
+    ok = np.abs(x) <= MAXF[fmt] * X
+    bound = np.maximum(np.abs(x) * 2.0 ** -(M + 1), X * 2.0 ** (emin - M - 1))
+    assert np.all(np.abs(y - x)[ok] <= bound[ok])
+
+
+def _exact_gemm_mx(orc, A, fa, sA, B, fb, sB):
+    ta = {c: Fraction(orc.decode(c, fa)) for c in range(256) if math.isfinite(orc.decode(c, fa))}
+    tb = {c: Fraction(orc.decode(c, fb)) for c in range(256) if math.isfinite(orc.decode(c, fb))}
+    M, K = A.shape
+    N = B.shape[0]
+    C = np.zeros((M, N))
+    D = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            c = Fraction(0)
+            d = Fraction(0)
+            for kb in range(K // 32):
+                coef = Fraction(2) ** (int(sA[m, kb]) + int(sB[n, kb]) - 254)
+                p = sum(ta[A[m, k]] * tb[B[n, k]] for k in range(32 * kb, 32 * kb + 32))
+                pa = sum(abs(ta[A[m, k]] * tb[B[n, k]]) for k in range(32 * kb, 32 * kb + 32))
+                c += coef * p
+                d += coef * pa
+            C[m, n] = float(c)
+            D[m, n] = float(d)
+    return C, D
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4), (E4, E5)])
+def test_gemm_mx_matches_exact_rationals(orc, fa, fb):
+    rng = np.random.default_rng(24)
+    M, N, K = 2, 16, 128
+    A = _rand_codes(rng, (M, K), fa)
+    B = _rand_codes(rng, (N, K), fb)
+    sA = rng.integers(100, 150, size=(M, K // 32)).astype(np.uint8)
+    sB = rng.integers(100, 150, size=(N, K // 32)).astype(np.uint8)
+    C, D = orc.gemm_mx(A, fa, sA, B, fb, sB)
+    Ce, De = _exact_gemm_mx(orc, A, fa, sA, B, fb, sB)
+    assert np.all(np.abs(C - Ce) <= 4 * 2.0 ** -52 * De)
+    assert np.allclose(D, De, rtol=1e-15, atol=0)
+
+
+def test_gemm_mx_unit_scales_is_integer_matmul(orc):
+    """Scale bytes 127 (2^0) and codes of small integers: an integer matmul."""
+    rng = np.random.default_rng(25)
+    ints = np.arange(-16, 17)
+    code = {0: 0x00}
+    for v in range(1, 17):
+        c = next(c for c in range(128) if orc.decode(c, E4) == v)
+        code[v], code[-v] = c, c | 0x80
+    Ai = rng.choice(ints, size=(8, 96))
+    Bi = rng.choice(ints, size=(40, 96))
+    A = np.vectorize(code.get)(Ai).astype(np.uint8)
+    B = np.vectorize(code.get)(Bi).astype(np.uint8)
+    C, _ = orc.gemm_mx(A, E4, np.full((8, 3), 127, np.uint8), B, E4, np.full((40, 3), 127, np.uint8))
+    assert np.array_equal(C, (Ai @ Bi.T).astype(np.float64))
