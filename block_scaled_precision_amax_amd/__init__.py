@@ -33,11 +33,14 @@ SYMBOLS = (
     "fp8q_quantize_1x128",
     "fp8q_quantize_1x128_t",
     "fp8q_quantize_128x128",
+    "fp8q_quantize_mx",
+    "fp8q_dequantize_mx",
     "fp8q_delayed_scaler_init",
     "fp8q_delayed_scaler_update",
     "fp8q_dequantize",
     "fp8q_gemm_blockscaled",
     "fp8q_gemm_blockscaled_fast",
+    "fp8q_gemm_mx",
 )
 
 
@@ -79,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "fp8q_quantize_1x128": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, vp]),
             "fp8q_quantize_1x128_t": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, vp]),
             "fp8q_quantize_128x128": (i32, [vp, i32, i64, i64, i64, i32, f32, vp, i64, vp, i64, vp]),
+            "fp8q_quantize_mx": (i32, [vp, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp]),
+            "fp8q_dequantize_mx": (i32, [vp, i32, i64, i64, i64, vp, i64, vp, i32, i64, vp]),
             "fp8q_delayed_scaler_init": (i32, [vp, i32, f32, f32, f32, vp]),
             "fp8q_delayed_scaler_update": (i32, [vp, vp, vp]),
             "fp8q_dequantize": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, i64, vp]),
@@ -86,6 +91,7 @@ def lib() -> ctypes.CDLL:
                                             vp, i32, i64, i64, i64, i64, vp]),
             "fp8q_gemm_blockscaled_fast": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64,
                                                  vp, i32, i64, i64, i64, i64, vp]),
+            "fp8q_gemm_mx": (i32, [vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp, i32, i64, i64, i64, i64, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -157,6 +163,16 @@ def fp8q_quantize_128x128(x, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, stre
                                        _ptr(scales), ld_s, _stream(stream, x)))
 
 
+def fp8q_quantize_mx(x, rows, cols, ldx, f, q, ldq, scales, ld_s, stream=None) -> None:
+    _check(lib().fp8q_quantize_mx(_ptr(x), _dt(x), rows, cols, ldx, f, _ptr(q), ldq, _ptr(scales), ld_s,
+                                  _stream(stream, x)))
+
+
+def fp8q_dequantize_mx(q, f, rows, cols, ldq, scales, ld_s, y, ldy, stream=None) -> None:
+    _check(lib().fp8q_dequantize_mx(_ptr(q), f, rows, cols, ldq, _ptr(scales), ld_s, _ptr(y), _dt(y), ldy,
+                                    _stream(stream, q)))
+
+
 def fp8q_delayed_scaler_init(state, window, max_val, eps, margin, stream=None) -> None:
     _check(lib().fp8q_delayed_scaler_init(_ptr(state), window, max_val, eps, margin, _stream(stream, state)))
 
@@ -181,3 +197,8 @@ def fp8q_gemm_blockscaled_fast(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb
     _check(lib().fp8q_gemm_blockscaled_fast(_ptr(A), fa, lda, _ptr(sA), sA_sm, sA_skb, _ptr(B), fb, ldb,
                                             _ptr(sB), gb, sB_sn, sB_skb, _ptr(C), _dt(C), ldc, M, N, K,
                                             _stream(stream, A)))
+
+
+def fp8q_gemm_mx(A, fa, lda, sA, ld_sa, B, fb, ldb, sB, ld_sb, C, ldc, M, N, K, stream=None) -> None:
+    _check(lib().fp8q_gemm_mx(_ptr(A), fa, lda, _ptr(sA), ld_sa, _ptr(B), fb, ldb, _ptr(sB), ld_sb, _ptr(C), _dt(C),
+                              ldc, M, N, K, _stream(stream, A)))

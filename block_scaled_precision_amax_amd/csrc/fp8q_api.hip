@@ -138,6 +138,34 @@ int fp8q_quantize_1x128_t(const void* x, fp8q_dtype dt, int64_t rows, int64_t co
   return launch_quantize_1x128_t(x, dt, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, S(stream));
 }
 
+int fp8q_quantize_mx(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx, fp8q_format f,
+                     uint8_t* q, int64_t ldq, uint8_t* scales, int64_t ld_s, void* stream) {
+  const char* fn = "quantize_mx";
+  if (!x || !q || !scales) return fail(FP8Q_EINVAL, "%s: null pointer", fn);
+  if (!valid_dt(dt) || !valid_fmt(f)) return fail(FP8Q_EINVAL, "%s: bad dtype or format", fn);
+  if (rows <= 0 || cols <= 0) return fail(FP8Q_EINVAL, "%s: rows and cols must be positive", fn);
+  if (cols % 32 != 0) return fail(FP8Q_ESHAPE, "%s: cols (%lld) must be a multiple of 32", fn, (long long)cols);
+  if (ldx < cols || ldq < cols || ld_s < cols / 32)
+    return fail(FP8Q_EINVAL, "%s: leading dimension smaller than the row", fn);
+  if (!aligned(x, 16) || !aligned(q, 16) || (ldx * esize(dt)) % 16 != 0 || ldq % 16 != 0)
+    return fail(FP8Q_EALIGN, "%s: x, q and their rows must be 16-byte aligned", fn);
+  return launch_quantize_mx(x, dt, rows, cols, ldx, f, q, ldq, scales, ld_s, S(stream));
+}
+
+int fp8q_dequantize_mx(const uint8_t* q, fp8q_format f, int64_t rows, int64_t cols, int64_t ldq,
+                       const uint8_t* scales, int64_t ld_s, void* y, fp8q_dtype out_dt, int64_t ldy, void* stream) {
+  const char* fn = "dequantize_mx";
+  if (!q || !scales || !y) return fail(FP8Q_EINVAL, "%s: null pointer", fn);
+  if (!valid_fmt(f) || !valid_dt(out_dt)) return fail(FP8Q_EINVAL, "%s: bad format or dtype", fn);
+  if (rows <= 0 || cols <= 0) return fail(FP8Q_EINVAL, "%s: rows and cols must be positive", fn);
+  if (cols % 32 != 0) return fail(FP8Q_ESHAPE, "%s: cols (%lld) must be a multiple of 32", fn, (long long)cols);
+  if (ldq < cols || ldy < cols || ld_s < cols / 32)
+    return fail(FP8Q_EINVAL, "%s: leading dimension smaller than the row", fn);
+  if (!aligned(q, 16) || !aligned(y, 16) || ldq % 8 != 0 || (ldy * esize(out_dt)) % 16 != 0)
+    return fail(FP8Q_EALIGN, "%s: q, y and their rows must be aligned (ldq % 8, y rows 16 bytes)", fn);
+  return launch_dequantize_mx(q, f, rows, cols, ldq, scales, ld_s, y, out_dt, ldy, S(stream));
+}
+
 int fp8q_quantize_128x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                           fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
                           int64_t ld_s, void* stream) {
@@ -213,6 +241,24 @@ int fp8q_gemm_blockscaled(const uint8_t* A, fp8q_format fa, int64_t lda, const f
                           int64_t N, int64_t K, void* stream) {
   return gemm_entry("gemm_blockscaled", A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb, sB_sn, sB_skb,
                     C, out_dt, ldc, M, N, K, false, stream);
+}
+
+int fp8q_gemm_mx(const uint8_t* A, fp8q_format fa, int64_t lda, const uint8_t* sA, int64_t ld_sa,
+                 const uint8_t* B, fp8q_format fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C,
+                 fp8q_dtype out_dt, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "gemm_mx";
+  if (!A || !sA || !B || !sB || !C) return fail(FP8Q_EINVAL, "%s: null pointer", fn);
+  if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_dt(out_dt)) return fail(FP8Q_EINVAL, "%s: bad format or dtype", fn);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(FP8Q_EINVAL, "%s: M, N, K must be positive", fn);
+  if (K % 128 != 0) return fail(FP8Q_ESHAPE, "%s: K (%lld) must be a multiple of 128", fn, (long long)K);
+  if (lda < K || ldb < K || ldc < N || ld_sa < K / 32 || ld_sb < K / 32)
+    return fail(FP8Q_EINVAL, "%s: leading dimension too small", fn);
+  if (!aligned(A, 16) || !aligned(B, 16) || lda % 16 != 0 || ldb % 16 != 0)
+    return fail(FP8Q_EALIGN, "%s: A, B and their leading dimensions must be 16-byte aligned", fn);
+  if (!aligned(sA, 4) || !aligned(sB, 4) || ld_sa % 4 != 0 || ld_sb % 4 != 0 ||
+      !aligned(C, out_dt == FP8Q_F32 ? 4 : 2))
+    return fail(FP8Q_EALIGN, "%s: scale rows must be 4-byte aligned; C aligned to its element", fn);
+  return launch_gemm_mx(A, fa, lda, sA, ld_sa, B, fb, ldb, sB, ld_sb, C, out_dt, ldc, M, N, K, S(stream));
 }
 
 int fp8q_gemm_blockscaled_fast(const uint8_t* A, fp8q_format fa, int64_t lda, const float* sA,

@@ -448,6 +448,160 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   }
 }
 
+// ---------------------------------------------------------------- MX GEMM
+// C = sum over 32-element K blocks of 2^(ea + eb) * (block sum of dec(a)
+// dec(b)), with E8M0 scales per row and block for A and B.  The scaled FP8
+// MFMA applies both scales itself, so the accumulators run over the whole
+// K with no promotion step.  Its 128-wide K operand is laid out so that
+// lane group q (= l/16) holds K positions 16q .. 16q+16 in its first four
+// registers and 64+16q .. 64+16q+16 in the last four, and the scale from
+// lane group g covers K positions 32g .. 32g+32 (measured on gfx950): each
+// lane therefore reads 16-byte chunks q and q+4 of its row, which keeps K
+// in memory order, and passes the scale of the 32-block g = q.  Tiling,
+// copies and tile order are those of the FP8 path (256x256 workgroup tile,
+// two LDS stages); the scale bytes of the tile's rows and columns (4 per
+// row and 128-wide K block) travel through LDS with the codes.
+template <int FA, int FB, int ODT>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ sA, int64_t ld_sa,
+    const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ sB, int64_t ld_sb,
+    void* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t ntm, int64_t ntn) {
+  constexpr int BM = 256, BN = 256, TI = 8, TJ = 4;
+  constexpr int NLOAD = BM / 64 + BN / 64 + 1;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2][BM * BK];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2][BN * BK];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sa[2][BM * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_sb[2][BN * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  int64_t tm, tn;
+  tile_of(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t nkb = K / BK;
+
+  uint32_t a_off[BM / 64], b_off[BN / 64];
+  dma_offsets<BM>(a_off, lda, m0, M, wave, lane);
+  dma_offsets<BN>(b_off, ldb, n0, N, wave, lane);
+  // scales: wavefronts 0-3 copy the 4 bytes (one dword) of A rows
+  // 64w + lane, wavefronts 4-7 those of B rows 64(w-4) + lane
+  const bool sc_a = wave < 4;
+  const int64_t sc_r = (sc_a ? m0 : n0) + 64 * (wave & 3) + lane;
+  const int64_t sc_lim = sc_a ? M : N;
+  const uint8_t* sc_row = sc_a ? sA + (sc_r < sc_lim ? sc_r : sc_lim - 1) * ld_sa
+                               : sB + (sc_r < sc_lim ? sc_r : sc_lim - 1) * ld_sb;
+
+  v4f acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int lr = lane & 15, lq = lane >> 4;
+  const int a_row0 = wm * TI * 16 + lr, b_row0 = wn * TJ * 16 + lr;
+  const int o0 = 16 * swz_chunk(lr, lq), o1 = 16 * swz_chunk(lr, lq + 4);
+
+  auto stage_block = [&](int64_t kb, int st) {
+    dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+    dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
+    uint8_t* dst = sc_a ? lds_sa[st] + 256 * (wave & 3) : lds_sb[st] + 256 * (wave & 3);
+    lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
+  };
+
+  auto compute = [&](int st) {
+    const uint8_t* la = lds_a[st] + a_row0 * BK;
+    const uint8_t* lb = lds_b[st] + b_row0 * BK;
+    auto frag = [&](const uint8_t* base) {
+      const u32x4 x0 = *(const u32x4*)(base + o0);
+      const u32x4 x1 = *(const u32x4*)(base + o1);
+      return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    };
+    v8i fb[TJ];
+    int sbj[TJ];
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      fb[j] = frag(lb + 16 * j * BK);
+      sbj[j] = lds_sb[st][(b_row0 + 16 * j) * 4 + lq];
+    }
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const v8i fa = frag(la + 16 * i * BK);
+      const int sai = lds_sa[st][(a_row0 + 16 * i) * 4 + lq];
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], FA, FB, 0, sai, 0, sbj[j]);
+    }
+  };
+
+  stage_block(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  int st = 0;
+  int64_t kb = 0;
+  for (; kb + 1 < nkb; ++kb) {
+    stage_block(kb + 1, st ^ 1);
+    compute(st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    st ^= 1;
+  }
+  compute(st);
+  (void)NLOAD;
+
+  // ---- epilogue: 16x16 results, column l%16, rows 4*(l/16) + e
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) {
+    const int64_t col = n0 + wn * TJ * 16 + 16 * j + lr;
+    if (col >= N) continue;
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t row = m0 + wm * TI * 16 + 16 * i + 4 * lq + e;
+        if (row >= M) continue;
+        if constexpr (ODT == FP8Q_F32)
+          __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
+        else
+          __builtin_nontemporal_store((uint16_t)f32_to_bf16(acc[i][j][e]), (uint16_t*)C + row * ldc + col);
+      }
+  }
+}
+
+template <int FA, int FB, int ODT>
+static void launch_mx_t(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
+                        int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C, int64_t ldc, int64_t M, int64_t N,
+                        int64_t K, hipStream_t st) {
+  const int64_t ntm = (M + 255) / 256, ntn = (N + 255) / 256;
+  hipLaunchKernelGGL((k_gemm_mx<FA, FB, ODT>), dim3((unsigned)(ntm * ntn)), dim3(kGemmThreads), 0, st, A, lda, sA,
+                     ld_sa, B, ldb, sB, ld_sb, C, ldc, M, N, K, ntm, ntn);
+}
+
+int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
+                   int fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C, int out_dt, int64_t ldc,
+                   int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "gemm_mx: more than 2^31-1 output tiles");
+  if ((M - 1) * lda + K > 0xFFFFFFFFll || (N - 1) * ldb + K > 0xFFFFFFFFll)
+    return fail(FP8Q_ESHAPE, "gemm_mx: an operand spans 4 GiB or more");
+#define FP8Q_MX_OUT(FA_, FB_)                                                                      \
+  if (out_dt == FP8Q_F32)                                                                          \
+    launch_mx_t<FA_, FB_, FP8Q_F32>(A, lda, sA, ld_sa, B, ldb, sB, ld_sb, C, ldc, M, N, K, st);    \
+  else                                                                                             \
+    launch_mx_t<FA_, FB_, FP8Q_BF16>(A, lda, sA, ld_sa, B, ldb, sB, ld_sb, C, ldc, M, N, K, st);
+  if (fa == FP8Q_E4M3FN && fb == FP8Q_E4M3FN) {
+    FP8Q_MX_OUT(0, 0)
+  } else if (fa == FP8Q_E5M2 && fb == FP8Q_E4M3FN) {
+    FP8Q_MX_OUT(1, 0)
+  } else if (fa == FP8Q_E4M3FN && fb == FP8Q_E5M2) {
+    FP8Q_MX_OUT(0, 1)
+  } else {
+    FP8Q_MX_OUT(1, 1)
+  }
+#undef FP8Q_MX_OUT
+  return check_launch("gemm_mx");
+}
+
 template <int FA, int FB, int GB, int ODT, bool FAST>
 static void launch_t(const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
                      const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn, int64_t sB_skb, void* C,

@@ -141,6 +141,10 @@ int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int
 int launch_quantize_1x128_t(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                             float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                             hipStream_t st);
+int launch_quantize_mx(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                       int64_t ldq, uint8_t* scales, int64_t ld_s, hipStream_t st);
+int launch_dequantize_mx(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq, const uint8_t* scales,
+                         int64_t ld_s, void* y, int out_dt, int64_t ldy, hipStream_t st);
 int launch_quantize_128x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                             float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                             hipStream_t st);
@@ -154,6 +158,10 @@ int launch_gemm(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t 
                 int64_t sA_skb, const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb,
                 int64_t sB_sn, int64_t sB_skb, void* C, int out_dt, int64_t ldc, int64_t M,
                 int64_t N, int64_t K, bool fast, hipStream_t st);
+
+int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
+                   int fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C, int out_dt, int64_t ldc,
+                   int64_t M, int64_t N, int64_t K, hipStream_t st);
 
 // Number of compute units of the current device (cached per device).
 int device_cu_count();

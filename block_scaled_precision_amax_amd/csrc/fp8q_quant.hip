@@ -660,6 +660,121 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- MX (microscaling) FP8
+// Blocks of 32 consecutive elements of a row share X = 2^e, e =
+// floor(log2 max|x|) - emax (emax 8 for E4M3, 15 for E5M2; clamped to
+// [-127, 127]), stored as the E8M0 byte e + 127; a block holding a NaN or an
+// Inf gets the NaN scale 0xFF and NaN codes; an all-zero block e = -127.
+// Codes are enc(x * 2^-e), a multiplication by a normal power of two, exact
+// wherever the code can be nonzero.  Each lane holds one 16-byte vector (8
+// bf16 or 4 fp32); the lanes of a block are consecutive (4 or 8) and reduce
+// the block maximum with xor shuffles.  Each workgroup walks a contiguous
+// chunk of vectors.
+template <int FMT>
+__device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
+  constexpr int kEmax = FMT == FP8Q_E4M3FN ? 8 : 15;
+  if (amax_bits == 0) return -127;
+  const int E = (int)(amax_bits >> 23);
+  const int fl = E > 0 ? E - 127 : (31 - __builtin_clz(amax_bits)) - 149;  // floor(log2 amax)
+  const int e = fl - kEmax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_mx(const void* __restrict__ x, int64_t vpr, int64_t nvec,
+                                                       int64_t ldx, uint8_t* __restrict__ q, int64_t ldq,
+                                                       uint8_t* __restrict__ scales, int64_t ld_s,
+                                                       int64_t per_wg) {
+  constexpr int VE = DT == FP8Q_F32 ? 4 : 8;   // elements per 16-byte vector
+  constexpr int LPB = 32 / VE;                 // lanes per block
+  constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
+  const char* xb = (const char*)x;
+  const int64_t v0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t v1 = v0 + per_wg < nvec ? v0 + per_wg : nvec;
+  for (int64_t base = v0; base < v1; base += kThreads) {
+    // vectors are counted along rows; blocks never straddle a row (cols % 32 == 0)
+    // and per_wg is a multiple of the block's lane count, so a block's lanes
+    // are always active together
+    const int64_t v = base + threadIdx.x;
+    const bool on = v < v1;
+    const int64_t r = on ? v / vpr : 0, c = on ? (v - r * vpr) * VE : 0;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (on) w = __builtin_nontemporal_load((const u32x4*)(xb + (r * ldx + c) * esz));
+    uint32_t m;
+    if constexpr (DT == FP8Q_F32)
+      m = max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
+    else
+      m = pk_fold(pk_absmax(pk_absmax(pk_absmax(pk_absmax(0u, w.x), w.y), w.z), w.w));
+#pragma unroll
+    for (int o = 1; o < LPB; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if (!on) continue;
+    uint8_t* qp = q + r * ldq + c;
+    const bool special = m >= 0x7F800000u;  // a NaN or an Inf in the block
+    if ((threadIdx.x & (LPB - 1)) == 0) scales[r * ld_s + (c >> 5)] = special ? 0xFF : (uint8_t)(mx_exponent<FMT>(m) + 127);
+    if (special) {
+      if constexpr (DT == FP8Q_F32) *(uint32_t*)qp = 0x7F7F7F7Fu;
+      else *(u32x2*)qp = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+      continue;
+    }
+    const float inv = __uint_as_float((uint32_t)(127 - mx_exponent<FMT>(m)) << 23);  // 2^-e, normal
+    if constexpr (DT == FP8Q_F32) {
+      const uint32_t o = pack4<FMT>(sat<FMT>(__uint_as_float(w.x) * inv), sat<FMT>(__uint_as_float(w.y) * inv),
+                                    sat<FMT>(__uint_as_float(w.z) * inv), sat<FMT>(__uint_as_float(w.w) * inv));
+      __builtin_nontemporal_store(o, (uint32_t*)qp);
+    } else {
+      u32x2 o;
+      o.x = pack4<FMT>(sat<FMT>(bf_lo(w.x) * inv), sat<FMT>(bf_hi(w.x) * inv), sat<FMT>(bf_lo(w.y) * inv),
+                       sat<FMT>(bf_hi(w.y) * inv));
+      o.y = pack4<FMT>(sat<FMT>(bf_lo(w.z) * inv), sat<FMT>(bf_hi(w.z) * inv), sat<FMT>(bf_lo(w.w) * inv),
+                       sat<FMT>(bf_hi(w.w) * inv));
+      __builtin_nontemporal_store(o, (u32x2*)qp);
+    }
+  }
+}
+
+// x^ = fl32(dec(q) * 2^(s - 127)) (NaN scale byte: NaN), as the block
+// dequantizer: 8 codes per lane, contiguous runs per instruction.
+template <int FMT, int ODT>
+__global__ __launch_bounds__(kThreads) void k_dequant_mx(const uint8_t* __restrict__ q, int64_t rows,
+                                                         int64_t cols, int64_t ldq,
+                                                         const uint8_t* __restrict__ scales, int64_t ld_s,
+                                                         void* __restrict__ y, int64_t ldy, int64_t per_wg) {
+  const int64_t gpr = cols / 8;  // 8-code groups per row
+  const int64_t total = rows * gpr;
+  const int64_t g0 = (int64_t)blockIdx.x * per_wg;
+  const int64_t g1 = g0 + per_wg < total ? g0 + per_wg : total;
+  for (int64_t g = g0 + threadIdx.x; g < g1; g += kThreads) {
+    const int64_t r = g / gpr, c = (g - r * gpr) * 8;
+    const uint32_t sb = scales[r * ld_s + (c >> 5)];
+    // 2^(sb-127): normal for sb >= 1, the subnormal 2^-127 for sb == 0
+    const float X = sb == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23);
+    const u32x2 w = *(const u32x2*)(q + r * ldq + c);
+    float o[8];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const float2 lo = dec2<FMT>(w[k], false), hi = dec2<FMT>(w[k], true);
+      o[4 * k] = canon_nan(lo.x * X);
+      o[4 * k + 1] = canon_nan(lo.y * X);
+      o[4 * k + 2] = canon_nan(hi.x * X);
+      o[4 * k + 3] = canon_nan(hi.y * X);
+    }
+    if (sb == 0xFF) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] = __uint_as_float(0x7FC00000u);
+    }
+    if constexpr (ODT == FP8Q_F32) {
+      float* yp = (float*)y + r * ldy + c;
+      *(u32x4*)yp = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+      *((u32x4*)yp + 1) = u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
+    } else {
+      uint32_t b[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) b[k] = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o[2 * k], (__bf16)o[2 * k + 1]});
+      *(u32x4*)((uint16_t*)y + r * ldy + c) = u32x4{b[0], b[1], b[2], b[3]};
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launches
 // Persistent grid for chunked streams: up to per_cu workgroups per CU.
 static int chunk_grid(int64_t chunks, int per_cu) {
@@ -812,6 +927,49 @@ int launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int
   if (fmt == FP8Q_E4M3FN) launch_dq_g<FP8Q_E4M3FN>(gran, out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
   else launch_dq_g<FP8Q_E5M2>(gran, out_dt, q, rows, cols, ldq, scales, ld_s, y, ldy, st);
   return check_launch("dequantize");
+}
+
+template <int DT, int FMT>
+static void launch_qmx(int grid, const void* x, int64_t vpr, int64_t nvec, int64_t ldx, uint8_t* q, int64_t ldq,
+                       uint8_t* scales, int64_t ld_s, int64_t per_wg, hipStream_t st) {
+  hipLaunchKernelGGL((k_quant_mx<DT, FMT>), dim3(grid), dim3(kThreads), 0, st, x, vpr, nvec, ldx, q, ldq, scales,
+                     ld_s, per_wg);
+}
+
+int launch_quantize_mx(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt, uint8_t* q,
+                       int64_t ldq, uint8_t* scales, int64_t ld_s, hipStream_t st) {
+  const int ve = dt == FP8Q_F32 ? 4 : 8;
+  const int64_t vpr = cols / ve, nvec = rows * vpr;
+  // contiguous chunks of whole thread-steps; a chunk is a multiple of 32
+  // elements' lanes, so no block is split between workgroups
+  const int64_t steps = (nvec + kThreads - 1) / kThreads;
+  const int grid = chunk_grid(steps, FP8Q_G_T);
+  const int64_t per_wg = ((steps + grid - 1) / grid) * kThreads;
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_qmx<FP8Q_F32, FP8Q_E4M3FN>(grid, x, vpr, nvec, ldx, q, ldq, scales, ld_s, per_wg, st);
+  else if (dt == FP8Q_F32) launch_qmx<FP8Q_F32, FP8Q_E5M2>(grid, x, vpr, nvec, ldx, q, ldq, scales, ld_s, per_wg, st);
+  else if (fmt == FP8Q_E4M3FN) launch_qmx<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, vpr, nvec, ldx, q, ldq, scales, ld_s, per_wg, st);
+  else launch_qmx<FP8Q_BF16, FP8Q_E5M2>(grid, x, vpr, nvec, ldx, q, ldq, scales, ld_s, per_wg, st);
+  return check_launch("quantize_mx");
+}
+
+template <int FMT, int ODT>
+static void launch_dqmx(int grid, const uint8_t* q, int64_t rows, int64_t cols, int64_t ldq, const uint8_t* scales,
+                        int64_t ld_s, void* y, int64_t ldy, int64_t per_wg, hipStream_t st) {
+  hipLaunchKernelGGL((k_dequant_mx<FMT, ODT>), dim3(grid), dim3(kThreads), 0, st, q, rows, cols, ldq, scales, ld_s, y,
+                     ldy, per_wg);
+}
+
+int launch_dequantize_mx(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq, const uint8_t* scales,
+                         int64_t ld_s, void* y, int out_dt, int64_t ldy, hipStream_t st) {
+  const int64_t total = rows * (cols / 8);
+  const int64_t steps = (total + kThreads - 1) / kThreads;
+  const int grid = chunk_grid(steps, FP8Q_G_D);
+  const int64_t per_wg = ((steps + grid - 1) / grid) * kThreads;
+  if (fmt == FP8Q_E4M3FN && out_dt == FP8Q_F32) launch_dqmx<FP8Q_E4M3FN, FP8Q_F32>(grid, q, rows, cols, ldq, scales, ld_s, y, ldy, per_wg, st);
+  else if (fmt == FP8Q_E4M3FN) launch_dqmx<FP8Q_E4M3FN, FP8Q_BF16>(grid, q, rows, cols, ldq, scales, ld_s, y, ldy, per_wg, st);
+  else if (out_dt == FP8Q_F32) launch_dqmx<FP8Q_E5M2, FP8Q_F32>(grid, q, rows, cols, ldq, scales, ld_s, y, ldy, per_wg, st);
+  else launch_dqmx<FP8Q_E5M2, FP8Q_BF16>(grid, q, rows, cols, ldq, scales, ld_s, y, ldy, per_wg, st);
+  return check_launch("dequantize_mx");
 }
 
 }  // namespace fp8q

@@ -130,6 +130,28 @@ int fp8q_quantize_1x128_t(const void* x, fp8q_dtype dt, int64_t rows, int64_t co
                           fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
                           int64_t ld_s, void* stream);
 
+/* MX (microscaling) FP8 quantization: every 32 consecutive elements of a
+ * row share one power-of-two scale X = 2^e held as an E8M0 byte e + 127
+ * (0xFF = NaN); [H] names this hardware-native block scaling as the next
+ * step after 1x128 / 128x128.  The conversion follows the OCP Microscaling
+ * Formats (MX) specification v1.0, 6.3: e = floor(log2 max|x|) - emax
+ * (emax = 8 for E4M3FN, 15 for E5M2), clamped to [-127, 127];
+ * q = enc(x / X), round to nearest even, clamped to +-MAX.  An all-zero
+ * block has e = -127; a block holding a NaN or an Inf gets scale byte 0xFF
+ * and codes 0x7F.
+ * x: rows x cols at x[r*ldx + c]; cols % 32 == 0; x and ldx*sizeof(dt)
+ *   16-B aligned.  q: codes at q[r*ldq + c], q and ldq 16-B aligned.
+ * scales: bytes at scales[r*ld_s + c/32], ld_s >= cols/32. */
+int fp8q_quantize_mx(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx, fp8q_format f,
+                     uint8_t* q, int64_t ldq, uint8_t* scales, int64_t ld_s, void* stream);
+
+/* MX dequantization y = fl32(dec(q) * 2^(s - 127)) (scale byte 0xFF: NaN,
+ * the quiet NaN 0x7FC00000), bf16 output as RNE of that fp32.  Layouts as
+ * fp8q_quantize_mx; cols % 32 == 0; q 16-B aligned with ldq % 8 == 0; y and
+ * its rows 16-B aligned. */
+int fp8q_dequantize_mx(const uint8_t* q, fp8q_format f, int64_t rows, int64_t cols, int64_t ldq,
+                       const uint8_t* scales, int64_t ld_s, void* y, fp8q_dtype out_dt, int64_t ldy, void* stream);
+
 /* Fine-grained 128x128 quantization of weights ([H] per_block(x, 128,
  * 128)).  As fp8q_quantize_1x128 with one scale per 128x128 tile:
  * scales[rb*ld_s + kb] for rows 128rb.. and columns 128kb..;
@@ -203,6 +225,20 @@ int fp8q_gemm_blockscaled_fast(const uint8_t* A, fp8q_format fa, int64_t lda, co
                                int64_t ldb, const float* sB, fp8q_gran gb, int64_t sB_sn,
                                int64_t sB_skb, void* C, fp8q_dtype out_dt, int64_t ldc, int64_t M,
                                int64_t N, int64_t K, void* stream);
+
+/* MX GEMM: C[m,n] = sum over 32-element K blocks kb of
+ *   2^(sA[m,kb] - 127) * 2^(sB[n,kb] - 127) * sum_{k in kb} dec(A[m,k]) dec(B[n,k]),
+ * the product of two fp8q_quantize_mx outputs (B as [N,K], K-contiguous).
+ * The scaled FP8 MFMA of gfx950 applies both scales and accumulates the
+ * whole K in fp32; like fp8q_gemm_blockscaled_fast it is bounded by
+ * |C - C_exact| <= 2^-10 * D, D the same sum over |terms|.
+ * A [M,K] codes, lda; B [N,K] codes, ldb (16-B aligned rows); sA [M, K/32]
+ * and sB [N, K/32] E8M0 bytes with row strides ld_sa, ld_sb (multiples of
+ * 4, >= K/32); K % 128 == 0; M, N free.  C [M,N] fp32 or bf16 (RNE), ldc.
+ * A scale byte 0xFF makes the result unspecified (NaN blocks). */
+int fp8q_gemm_mx(const uint8_t* A, fp8q_format fa, int64_t lda, const uint8_t* sA, int64_t ld_sa,
+                 const uint8_t* B, fp8q_format fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C,
+                 fp8q_dtype out_dt, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream);
 
 #ifdef __cplusplus
 }

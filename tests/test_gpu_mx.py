@@ -1,0 +1,255 @@
+"""GPU parity of the MX (OCP microscaling) FP8 path against the CPU oracle.
+
+Quantize: 32-element row blocks, one E8M0 scale byte per block; codes and
+scale bytes must equal the oracle's bit for bit, for fp32 and bf16 inputs,
+both formats, ragged and strided shapes and blocks that take every branch
+(zero, NaN, Inf, fp32 denormals, clamped exponents, rounding midpoints).
+Dequantize: bit-exact fp32 (the product of a code and a power of two is
+exact unless it overflows) and its round-to-nearest-even bf16.
+GEMM: the scaled FP8 MFMA accumulates in fp32; the bar is
+|C - C_exact| <= 2^-10 * D with D the sum of the terms' magnitudes, for
+scales that keep every scaled term in fp32's normal range.
+All calls go through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_precision_amax_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+E4, E5 = 0, 1
+MX_TOL = 2.0 ** -10
+
+
+def assert_equal_bytes(got, want, what=""):
+    got = np.ascontiguousarray(got).reshape(-1)
+    want = np.ascontiguousarray(want).reshape(-1)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"{what}: {bad.size} differ, first at {bad[0]}: {got[bad[0]]:#x} vs {want[bad[0]]:#x}"
+
+
+def run_quant(fq, x_dev, rows, cols, ldx, fmt, pad_q=0, pad_s=0):
+    ldq, ld_s = cols + pad_q, cols // 32 + pad_s
+    q = torch.full((rows, ldq), 0xAA, dtype=torch.uint8, device=x_dev.device)
+    s = torch.full((rows, ld_s), 0x55, dtype=torch.uint8, device=x_dev.device)
+    fq.fp8q_quantize_mx(x_dev, rows, cols, ldx, fmt, q, ldq, s, ld_s)
+    torch.cuda.synchronize()
+    qn, sn = q.cpu().numpy(), s.cpu().numpy()
+    if pad_q:
+        assert np.all(qn[:, cols:] == 0xAA), "wrote past the code row"
+    if pad_s:
+        assert np.all(sn[:, cols // 32:] == 0x55), "wrote past the scale row"
+    return qn[:, :cols], sn[:, :cols // 32]
+
+
+def oracle_input(x, rows, cols):
+    """The rows x cols view of x as the oracle's input (fp32, or bf16 bits)."""
+    return np.ascontiguousarray(W.to_numpy_input(x.cpu())[:rows, :cols])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("rows,cols,padx,padq,pads", [(1, 32, 0, 0, 0), (7, 96, 0, 0, 0), (300, 1024, 0, 0, 0),
+                                                       (129, 7168, 0, 0, 0), (33, 160, 32, 16, 3),
+                                                       (64, 4096, 64, 32, 8)])
+def test_quantize_mx_random(fq, orc, gpu, dtype, fmt, rows, cols, padx, padq, pads):
+    """Activation-like data (N(0,1) with outlier columns x1e3), ragged row
+    counts, one-block rows and padded leading dimensions."""
+    x = W.activation(rows, cols + padx, seed=rows * 7 + cols, factor=1e3, dtype=dtype, device=gpu)
+    q, s = run_quant(fq, x, rows, cols, cols + padx, fmt, padq, pads)
+    wq, ws = orc.quantize_mx(oracle_input(x, rows, cols), fmt)
+    assert_equal_bytes(s, ws, "scale bytes")
+    assert_equal_bytes(q, wq, "codes")
+
+
+def special_blocks(rng, rows):
+    """rows x 512 fp32: each 32-wide block takes one branch of the encoder."""
+    x = rng.standard_normal((rows, 512)).astype(np.float32)
+    x[:, 0:32] = 0.0                                   # zero block: scale byte 0
+    x[::2, 0:32] = -0.0
+    x[0, 40] = np.nan                                  # NaN block: 0xFF / 0x7F
+    x[1, 41] = np.inf
+    x[2, 42] = -np.inf
+    x[3, 43] = -np.nan
+    x[:, 64:96] = (rng.standard_normal((rows, 32)) * 1e-42).astype(np.float32)  # fp32 denormals, e clamps to -127
+    x[:, 96:128] = (rng.standard_normal((rows, 32)) * 1e-38).astype(np.float32)  # amax near the normal edge
+    x[:, 128:160] = (rng.standard_normal((rows, 32)) * 1e37).astype(np.float32)
+    x[::2, 128:160] = np.float32(3.4e38)               # largest exponents
+    # exact powers of two as amax (floor(log2) on the boundary) and values
+    # just below them
+    p = 2.0 ** rng.integers(-20, 20, size=(rows, 1))
+    x[:, 160:192] = (rng.uniform(-1, 1, size=(rows, 32)) * p).astype(np.float32)
+    x[:, 160] = p[:, 0].astype(np.float32)
+    x[:, 192:224] = (rng.uniform(-1, 1, size=(rows, 32)) * p).astype(np.float32)
+    x[:, 192] = np.nextafter(np.float32(p[:, 0]), np.float32(0))
+    # rounding midpoints of both formats after the power-of-two scaling
+    mids = np.array([(1 + (m + 0.5) / 8) * 2.0 ** e for e in range(-6, 8) for m in range(8)], dtype=np.float32)
+    k = rng.integers(0, mids.size, size=(rows, 31))
+    ulp = rng.integers(-1, 2, size=(rows, 31)).astype(np.int32)
+    x[:, 224:255] = (mids[k].view(np.int32) + ulp).view(np.float32) * np.where(rng.random((rows, 31)) < .5, -1, 1)
+    x[:, 255] = np.float32(256.0)
+    x[:, 256:288] = np.float32(1.0) * np.sign(rng.standard_normal((rows, 32))).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_mx_special_values(fq, orc, gpu, dtype, fmt):
+    rng = np.random.default_rng(77 + fmt)
+    x = torch.from_numpy(special_blocks(rng, 96)).to(dtype)
+    xd = x.to(gpu)
+    q, s = run_quant(fq, xd, 96, 512, 512, fmt)
+    wq, ws = orc.quantize_mx(oracle_input(x, 96, 512), fmt)
+    assert_equal_bytes(s, ws, "scale bytes")
+    assert_equal_bytes(q, wq, "codes")
+    assert np.all(s[:, 0] == 0) and np.all(s[0:4, 1] == 0xFF)
+
+
+def test_quantize_mx_full_activation(fq, orc, gpu):
+    """The 16384 x 7168 bf16 activation of the layer, compared on sampled rows."""
+    R, Cc = 16384, 7168
+    x = W.activation(R, Cc, seed=4, factor=1e3, dtype=torch.bfloat16, device=gpu)
+    q, s = run_quant(fq, x, R, Cc, Cc, E4)
+    rows = np.unique(np.concatenate([np.linspace(0, R - 1, 64).astype(np.int64), [R - 1]]))
+    xs = W.to_numpy_input(x[torch.from_numpy(rows).to(gpu)].cpu())
+    wq, ws = orc.quantize_mx(xs, E4)
+    assert_equal_bytes(s[rows], ws, "scale bytes")
+    assert_equal_bytes(q[rows], wq, "codes")
+
+
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("rows,cols,padq,pads,pady", [(5, 64, 0, 0, 0), (257, 1024, 16, 2, 8), (64, 4096, 0, 0, 0)])
+def test_dequantize_mx(fq, orc, gpu, out, fmt, rows, cols, padq, pads, pady):
+    """Every finite code and every scale byte 0..254 (with 0xFF NaN blocks
+    mixed in): overflow to Inf, fp32 subnormal results, exact products."""
+    q = W.fp8_codes((rows, cols + padq), fmt, seed=rows + cols)
+    g = torch.Generator().manual_seed(rows * 3 + cols)
+    s = torch.randint(0, 255, (rows, cols // 32 + pads), generator=g, dtype=torch.int32).to(torch.uint8)
+    s[0, 0] = 0xFF
+    s[-1, -1 - pads] = 0
+    y = torch.full((rows, cols + pady), -3.0, dtype=out, device=gpu)
+    fq.fp8q_dequantize_mx(q.to(gpu), fmt, rows, cols, cols + padq, s.to(gpu), cols // 32 + pads, y, cols + pady)
+    torch.cuda.synchronize()
+    y = y.cpu()
+    if pady:
+        assert torch.all(y[:, cols:] == -3.0)
+    want = torch.from_numpy(orc.dequantize_mx(q[:, :cols].numpy(), fmt, s[:, :cols // 32].numpy()))
+    got = y[:, :cols]
+    if out == torch.bfloat16:
+        # NaN blocks hold the canonical quiet NaN 0x7FC0 (torch's own cast
+        # may pick another NaN pattern)
+        w16 = want.to(torch.bfloat16).view(torch.int16).clone()
+        w16[torch.isnan(want)] = 0x7FC0
+        assert_equal_bytes(got.view(torch.int16).numpy(), w16.numpy(), "bf16")
+    else:
+        assert_equal_bytes(got.view(torch.int32).numpy(), want.view(torch.int32).numpy(), "fp32")
+
+
+# ------------------------------------------------------------------ GEMM
+def run_gemm_mx(fq, A, fa, sA, B, fb, sB, out=torch.float32, pad=(0, 0, 0, 0, 0), dev="cuda"):
+    """A [M,K], B [N,K] codes and [.., K/32] scale bytes, copied into padded
+    device buffers (pads of lda, ldb, ld_sa, ld_sb, ldc)."""
+    M, K = A.shape
+    N = B.shape[0]
+    pa, pb, psa, psb, pc = pad
+
+    def padded(t, p):
+        buf = torch.full((t.shape[0], t.shape[1] + p), 0x41, dtype=torch.uint8, device=dev)
+        buf[:, :t.shape[1]] = t.to(dev)
+        return buf
+
+    Ad, Bd, sAd, sBd = padded(A, pa), padded(B, pb), padded(sA, psa), padded(sB, psb)
+    C = torch.full((M, N + pc), float("nan"), dtype=out, device=dev)
+    fq.fp8q_gemm_mx(Ad, fa, K + pa, sAd, K // 32 + psa, Bd, fb, K + pb, sBd, K // 32 + psb, C, N + pc, M, N, K)
+    torch.cuda.synchronize()
+    C = C.cpu()
+    if pc:
+        assert torch.all(torch.isnan(C[:, N:])), "wrote past the output row"
+    return C[:, :N]
+
+
+def rand_e8m0(shape, seed, lo=117, hi=138):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, hi, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+
+
+def check_mx(C, Cref, D, what=""):
+    C = C.to(torch.float64).numpy()
+    assert np.all(np.isfinite(C)), what
+    err = np.abs(C - Cref)
+    ratio = np.where(D > 0, err / np.where(D > 0, D, 1), np.where(err > 0, np.inf, 0))
+    worst = float(ratio.max())
+    assert worst <= MX_TOL, f"{what}: max |dC|/D = {worst:.3e}"
+    return worst
+
+
+@pytest.mark.parametrize("fa,fb", [(E4, E4), (E5, E4), (E4, E5), (E5, E5)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (64, 128, 128), (1, 256, 256), (300, 200, 384), (513, 260, 1024)])
+def test_gemm_mx_random_codes(fq, orc, gpu, fa, fb, M, N, K):
+    """Uniformly random finite codes over the whole code space and random
+    scale bytes 2^-10 .. 2^10; ragged M and N (partial tiles), one and
+    several K tiles.  The bf16 output is the RNE of the fp32 one."""
+    A = W.fp8_codes((M, K), fa, seed=M + K)
+    B = W.fp8_codes((N, K), fb, seed=N + K + 1)
+    sA = rand_e8m0((M, K // 32), 11 + M)
+    sB = rand_e8m0((N, K // 32), 12 + N)
+    C = run_gemm_mx(fq, A, fa, sA, B, fb, sB)
+    Cref, D = orc.gemm_mx(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy())
+    check_mx(C, Cref, D, f"{M}x{N}x{K}")
+    Cb = run_gemm_mx(fq, A, fa, sA, B, fb, sB, out=torch.bfloat16)
+    assert torch.equal(Cb.view(torch.int16), C.to(torch.bfloat16).view(torch.int16))
+
+
+def test_gemm_mx_strided(fq, orc, gpu):
+    M, N, K = 130, 300, 640
+    A = W.fp8_codes((M, K), E4, seed=5)
+    B = W.fp8_codes((N, K), E4, seed=6)
+    sA = rand_e8m0((M, K // 32), 7)
+    sB = rand_e8m0((N, K // 32), 8)
+    C = run_gemm_mx(fq, A, E4, sA, B, E4, sB, pad=(32, 128, 4, 12, 5))
+    Cref, D = orc.gemm_mx(A.numpy(), E4, sA.numpy(), B.numpy(), E4, sB.numpy())
+    check_mx(C, Cref, D, "strided")
+
+
+def test_gemm_mx_block_scales_distinct(fq, orc, gpu):
+    """Every 32-block of K carries its own scale: one nonzero block per
+    output row/column pair must be scaled by exactly its own bytes (a
+    mapping of scales to the wrong K positions fails this exactly)."""
+    M, N, K = 64, 64, 256
+    A = torch.zeros(M, K, dtype=torch.uint8)
+    B = torch.zeros(N, K, dtype=torch.uint8)
+    for m in range(M):
+        A[m, 32 * (m % 8) + (m * 5) % 32] = 0x38  # 1.0 in E4M3
+    for n in range(N):
+        B[n, 32 * (n % 8):32 * (n % 8) + 32] = 0x40  # 2.0
+    sA = rand_e8m0((M, K // 32), 21, 100, 150)
+    sB = rand_e8m0((N, K // 32), 22, 100, 150)
+    C = run_gemm_mx(fq, A, E4, sA, B, E4, sB)
+    Cref, D = orc.gemm_mx(A.numpy(), E4, sA.numpy(), B.numpy(), E4, sB.numpy())
+    assert np.array_equal(C.to(torch.float64).numpy(), Cref)
+    assert np.count_nonzero(Cref) == M * N // 8
+
+
+def test_gemm_mx_quantized_layer_sampled(fq, orc, gpu):
+    """The layer's shape, 16384 x 18432 x 7168: the bf16 activation and the
+    weight quantized on the GPU by fp8q_quantize_mx (E4M3FN), fp32 output
+    on 16 sampled rows against the oracle."""
+    M, N, K = 16384, 18432, 7168
+    x = W.activation(M, K, seed=4, factor=1e3, dtype=torch.bfloat16, device=gpu)
+    w = W.weight(N, K, seed=40, device=gpu)
+    qa = torch.empty(M, K, dtype=torch.uint8, device=gpu)
+    sa = torch.empty(M, K // 32, dtype=torch.uint8, device=gpu)
+    qb = torch.empty(N, K, dtype=torch.uint8, device=gpu)
+    sb = torch.empty(N, K // 32, dtype=torch.uint8, device=gpu)
+    fq.fp8q_quantize_mx(x, M, K, K, E4, qa, K, sa, K // 32)
+    fq.fp8q_quantize_mx(w, N, K, K, E4, qb, K, sb, K // 32)
+    C = torch.empty(M, N, dtype=torch.float32, device=gpu)
+    fq.fp8q_gemm_mx(qa, E4, K, sa, K // 32, qb, E4, K, sb, K // 32, C, N, M, N, K)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.linspace(0, M - 1, 16).astype(np.int64), [M - 1]]))
+    ri = torch.from_numpy(rows).to(gpu)
+    Cref, D = orc.gemm_mx(qa[ri].cpu().numpy(), E4, sa[ri].cpu().numpy(), qb.cpu().numpy(), E4, sb.cpu().numpy())
+    check_mx(C[ri].cpu(), Cref, D, "layer")
