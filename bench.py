@@ -70,6 +70,7 @@ def algorithmic():
         "quantize_tensor_bytes": n * 2 + n + 4,            # bf16 read, codes written, amax
         "dequantize_bytes": n + 2 * n + 4,                  # codes read, bf16 written, scale
         "quantize_1x128_bytes": nx * 2 + nx + 4 * nx // 128,  # bf16 read, codes + scales written
+        "quantize_mx_bytes": nx * 2 + nx + nx // 32,     # bf16 in, codes + E8M0 bytes (same for dequantize)
         "gemm_flop": 2 * LM * LN * LK,
         # codes of A and B, their scales, bf16 C
         "gemm_bytes": LM * LK + LN * LK + 4 * (LM * (LK // 128) + (LN // 128) * (LK // 128)) + 2 * LM * LN,
@@ -260,6 +261,29 @@ def run_gpu(steps: int, warmup: int):
     del dyt, sdyt, xt, sxt, Xa
     torch.cuda.empty_cache()
 
+    # MX FP8 (32-element blocks, E8M0 scales) on the layer's shapes: the bf16
+    # activation quantized, dequantized, and the MX GEMM against the weight
+    Xm = inputs["X"]
+    qm = torch.empty(LM, LK, dtype=torch.uint8, device=dev)
+    sm = torch.empty(LM, LK // 32, dtype=torch.uint8, device=dev)
+    per["quantize_mx"] = per_launch(lambda r: fq.fp8q_quantize_mx(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, qm, LK, sm,
+                                                                  LK // 32), 16)
+    ym = torch.empty(LM, LK, dtype=torch.bfloat16, device=dev)
+    per["dequantize_mx"] = per_launch(lambda r: fq.fp8q_dequantize_mx(qm, fq.E4M3FN, LM, LK, LK, sm, LK // 32, ym, LK),
+                                      16)
+    del ym
+    wm = W.weight(LN, LK, seed=40, device=dev)
+    qwm = torch.empty(LN, LK, dtype=torch.uint8, device=dev)
+    swm = torch.empty(LN, LK // 32, dtype=torch.uint8, device=dev)
+    fq.fp8q_quantize_mx(wm, LN, LK, LK, fq.E4M3FN, qwm, LK, swm, LK // 32)
+    del wm
+    fq.fp8q_quantize_mx(Xm, LM, LK, LK, fq.E4M3FN, qm, LK, sm, LK // 32)
+    Cm = torch.empty(LM, LN, dtype=torch.bfloat16, device=dev)
+    per["gemm_mx"] = per_launch(lambda r: fq.fp8q_gemm_mx(qm, fq.E4M3FN, LK, sm, LK // 32, qwm, fq.E4M3FN, LK, swm,
+                                                          LK // 32, Cm, LN, LM, LN, LK), 8)
+    del qm, sm, qwm, swm, Cm
+    torch.cuda.empty_cache()
+
     # Copy reference: a plain elementwise pass (fp32 negation) over 1 GiB,
     # the yardstick for the streaming kernels and the calibration of the
     # HBM byte counters.
@@ -356,6 +380,9 @@ def main():
     q_1 = gbps(alg["quantize_1x128_bytes"], per["quantize_1x128"])
     dq = gbps(alg["dequantize_bytes"], per["dequantize_x"])
     cp = gbps(8 * COPY_ELEMS, per["copy_reference"])
+    q_mx = gbps(alg["quantize_mx_bytes"], per["quantize_mx"])
+    dq_mx = gbps(alg["quantize_mx_bytes"], per["dequantize_mx"])
+    mx_tflops = alg["gemm_flop"] / (per["gemm_mx"] * 1e-3) / 1e12
     traffic = measured_traffic()
     out = {
         "metric": "quantize GB/s + block-scaled FP8 GEMM TFLOPS, % of HBM / FP8-MFMA peak",
@@ -409,6 +436,14 @@ def main():
                                                                  "E5M2 x E4M3FN, 1x128 A / 128x128 B scales, fp32 out"),
             "gemm_blockscaled_wgrad_4096x4096x16384": gemm_entry(per["gemm_wgrad"], 4096, 4096, 16384,
                                                                  "E5M2 x E4M3FN, 1x128 A and B scales, fp32 out"),
+            "quantize_mx_bf16": {"ms": round(per["quantize_mx"], 4), "GB/s": round(q_mx, 1),
+                                 "frac_hbm": round(q_mx / HBM_PEAK_GBPS, 4),
+                                 "note": "MX E4M3FN, 32-element blocks, E8M0 scales; the layer's activation"},
+            "dequantize_mx_bf16": {"ms": round(per["dequantize_mx"], 4), "GB/s": round(dq_mx, 1),
+                                   "frac_hbm": round(dq_mx / HBM_PEAK_GBPS, 4)},
+            "gemm_mx": {"ms": round(per["gemm_mx"], 4), "TFLOP/s": round(mx_tflops, 2),
+                        "frac_fp8_peak": round(mx_tflops / FP8_PEAK_TFLOPS, 4),
+                        "operands": "MX E4M3FN x MX E4M3FN, scaled FP8 MFMA, bf16 out, the layer's shape"},
             "copy_reference_fp32": {"ms": round(per["copy_reference"], 4), "GB/s": round(cp, 1),
                                     "frac_hbm": round(cp / HBM_PEAK_GBPS, 4),
                                     "note": "torch elementwise pass, 1 GiB in + 1 GiB out: attainable streaming rate"},
