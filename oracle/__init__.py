@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
             "orc_quantize_blocks": (None, [vp, i32, i64, i64, i64, i64, i64, i32, f32, vp, i64, vp, i64]),
             "orc_dequantize": (None, [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, i64]),
             "orc_scaler_init": (i32, [vp, i32, f32, f32, f32]),
+            "orc_scaler_init_stat": (i32, [vp, i32, f32, f32, f32, i32, f32]),
             "orc_scaler_update": (None, [vp, f32]),
             "orc_scaler_size": (i64, []),
             "orc_gemm_blockscaled": (None, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64,
@@ -186,16 +187,22 @@ def rel_err(qhat: np.ndarray, x: np.ndarray) -> float:
 class Scaler(ctypes.Structure):
     _fields_ = [("ring", ctypes.c_float * 1024), ("window", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("pos", ctypes.c_int32), ("max_val", ctypes.c_float), ("eps", ctypes.c_float),
-                ("margin", ctypes.c_float), ("scale", ctypes.c_float)]
+                ("margin", ctypes.c_float), ("scale", ctypes.c_float), ("stat", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("pad_", ctypes.c_int32), ("ema", ctypes.c_double)]
 
 
-def scaler_new(window: int, fmt: int, eps: float = EPS, margin: float = 1.0) -> Scaler:
+STAT_MAX, STAT_MEAN, STAT_EMA = 0, 1, 2
+
+
+def scaler_new(window: int, fmt: int, eps: float = EPS, margin: float = 1.0, stat: int = STAT_MAX,
+               alpha: float = 0.0) -> Scaler:
+    """A delayed scaler ([A] 4.2): window statistic max (default), mean, or EMA with coefficient alpha."""
     st = Scaler()
     assert ctypes.sizeof(st) == lib().orc_scaler_size()
-    rc = lib().orc_scaler_init(ctypes.addressof(st), window, MAX_FINITE[fmt], float(np.float32(eps)),
-                               float(np.float32(margin)))
+    rc = lib().orc_scaler_init_stat(ctypes.addressof(st), window, MAX_FINITE[fmt], float(np.float32(eps)),
+                                    float(np.float32(margin)), stat, float(np.float32(alpha)))
     if rc:
-        raise ValueError("window must be in [1, 1024]")
+        raise ValueError("window must be in [1, 1024], stat in {0, 1, 2}, alpha in (0, 1] for the EMA")
     return st
 
 

@@ -244,41 +244,94 @@ void orc_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64
 /* ------------------------------------------------------------------ */
 /* delayed scaling ([A] 4.2 DelayedScaler): a window of the last    */
 /* `window` amax values; once it is full, the scale becomes             */
-/* scale(max(window)); until then it stays at its initial 1.0.  The     */
+/* scale(stat(window)); until then it stays at its initial 1.0.  The    */
 /* scale in force at step t quantizes x_t; amax(x_t) is pushed after.   */
+/* stat ([A] 4.2: the window maximum, the mean as a gentler option, and */
+/* the exponential moving average that smooths amax changes; [A] 4.3):  */
+/*   0 max of the window;                                               */
+/*   1 mean of the window: the window's values summed in fp64 by        */
+/*     pairwise (binary-tree) summation over the 1024 slots, unused      */
+/*     slots 0, divided by `window` in fp64, rounded to fp32;            */
+/*   2 EMA: e_1 = amax_1, e_t = alpha*amax_t + (1-alpha)*e_{t-1}, each   */
+/*     product and the sum rounded to fp64, e kept in fp64; the scale    */
+/*     uses fl32(e).  The window only sets when the scale first moves.  */
+/* NaN: max and mean propagate a NaN while it is in the window; the     */
+/* EMA keeps it for good.                                               */
 /* ------------------------------------------------------------------ */
 typedef struct {
   float ring[1024];
   int32_t window, count, pos;
   float max_val, eps, margin;
   float scale;
+  int32_t stat;
+  float alpha;
+  int32_t pad_;
+  double ema;
 } orc_scaler;
 
-int orc_scaler_init(orc_scaler* st, int32_t window, float max_val, float eps, float margin) {
+int orc_scaler_init_stat(orc_scaler* st, int32_t window, float max_val, float eps, float margin, int32_t stat,
+                         float alpha) {
   if (window < 1 || window > 1024) return 1;
+  if (stat < 0 || stat > 2) return 1;
+  if (stat == 2 && !(alpha > 0.0f && alpha <= 1.0f)) return 1;
   memset(st, 0, sizeof(*st));
   st->window = window;
   st->max_val = max_val;
   st->eps = eps;
   st->margin = margin;
   st->scale = 1.0f;
+  st->stat = stat;
+  st->alpha = stat == 2 ? alpha : 0.0f;
   return 0;
 }
 
+int orc_scaler_init(orc_scaler* st, int32_t window, float max_val, float eps, float margin) {
+  return orc_scaler_init_stat(st, window, max_val, eps, margin, 0, 0.0f);
+}
+
+/* pairwise sum of n (a power of two) fp64 values */
+static double pairwise_sum(const double* v, int n) {
+  if (n == 1) return v[0];
+  double left = pairwise_sum(v, n / 2);
+  double right = pairwise_sum(v + n / 2, n / 2);
+  return left + right;
+}
+
 void orc_scaler_update(orc_scaler* st, float amax) {
+  int first = st->count == 0;
   st->ring[st->pos] = amax;
   st->pos = (st->pos + 1) % st->window;
   if (st->count < st->window) st->count += 1;
-  if (st->count >= st->window) {
-    float m = 0.0f;
+  if (st->stat == 2) {
+    if (first) {
+      st->ema = (double)amax;
+    } else {
+      double a = (double)st->alpha;
+      double t1 = a * (double)amax;
+      double t2 = (1.0 - a) * st->ema;
+      st->ema = t1 + t2;
+    }
+  }
+  if (st->count < st->window) return;
+  float m;
+  if (st->stat == 0) {
+    m = 0.0f;
     int has_nan = 0;
     for (int32_t i = 0; i < st->window; ++i) {
       if (isnan(st->ring[i])) has_nan = 1;
       else if (st->ring[i] > m) m = st->ring[i];
     }
     if (has_nan) m = canonical_nan();
-    st->scale = orc_scale(m, st->max_val, st->eps, st->margin);
+  } else if (st->stat == 1) {
+    double v[1024];
+    for (int i = 0; i < 1024; ++i) v[i] = i < st->window ? (double)st->ring[i] : 0.0;
+    double mean = pairwise_sum(v, 1024) / (double)st->window;
+    m = (float)mean;
+  } else {
+    m = (float)st->ema;
   }
+  if (isnan(m)) m = canonical_nan();
+  st->scale = orc_scale(m, st->max_val, st->eps, st->margin);
 }
 
 int64_t orc_scaler_size(void) { return (int64_t)sizeof(orc_scaler); }

@@ -369,6 +369,107 @@ def test_window_one_is_current_scaling(orc):
         orc.scaler_new(0, E4)
 
 
+def fl32_of(fr: Fraction) -> np.float32:
+    """Round an exact rational to the nearest fp32, ties to even (by exact
+    comparison with the neighbouring floats, no double rounding)."""
+    c = np.float32(float(fr))
+    best = None
+    for v in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        d = abs(Fraction(float(v)) - fr)
+        if best is None or d < best[0] or (d == best[0] and (int(v.view(np.uint32)) & 1) == 0):
+            best = (d, v)
+    return best[1]
+
+
+def test_scaler_mean_of_window_closed_forms(orc):
+    """Window mean ([A] 4.2 names the mean as the gentler choice): a ramp
+    amax_t = t + 1 gives the mean (2t - W + 3)/2 of the last W values, a
+    constant gives the constant; the scale is fl32(fl32(mean)*margin)/MAX and
+    stays 1.0 until the window is full."""
+    for W in (1, 5, 16, 1024):
+        st = orc.scaler_new(W, E4, stat=orc.STAT_MEAN, margin=1.1)
+        for t in range(W + 40):
+            used = st.scale
+            if t < W:
+                assert used == 1.0
+            else:
+                # values 1..t in the ring, the last W of them are t-W+1 .. t
+                mean = Fraction(sum(range(t - W + 1, t + 1)), W)
+                want = f32(f32(fl32_of(mean)) * f32(1.1)) / f32(448.0)
+                assert used == want, (W, t)
+            orc.scaler_update(st, float(t + 1))
+
+
+def test_scaler_mean_random_windows_match_exact_mean(orc):
+    """For random amax histories of every magnitude the mean statistic is the
+    exact rational mean rounded once to fp32 (the fp64 pairwise sum is far
+    more precise than the fp32 result)."""
+    rng = np.random.default_rng(31)
+    for trial in range(60):
+        W = int(rng.integers(1, 1025))
+        st = orc.scaler_new(W, E5, stat=orc.STAT_MEAN)
+        vals = (np.exp(rng.normal(0, 6, size=W + int(rng.integers(0, 50))))).astype(np.float32)
+        for v in vals:
+            orc.scaler_update(st, float(v))
+        last = vals[-W:]
+        mean = sum((Fraction(float(v)) for v in last), Fraction(0)) / W
+        m = fl32_of(mean)
+        assert st.scale == max(m, f32(orc.EPS)) / f32(57344.0), trial
+        assert st.scale <= max(last.max(), f32(orc.EPS)) / f32(57344.0)
+
+
+def test_scaler_mean_nan_leaves_with_the_window(orc):
+    st = orc.scaler_new(4, E4, stat=orc.STAT_MEAN)
+    seq = [1.0, 2.0, float("nan"), 3.0, 4.0, 5.0, 6.0, 7.0]
+    for t, a in enumerate(seq):
+        orc.scaler_update(st, a)
+        if 3 <= t <= 5:
+            assert np.isnan(st.scale)
+    assert st.scale == f32(5.5) / f32(448.0)
+
+
+def test_scaler_ema_closed_forms(orc):
+    """EMA ([A] 4.2: smoothing of amax over the history): alpha = 1/2 after
+    one value A and then zeros halves exactly each step, e_t = A*2^-t; alpha
+    = 1 is current scaling; a constant history keeps the constant."""
+    st = orc.scaler_new(1, E4, stat=orc.STAT_EMA, alpha=0.5)
+    A = 3000.0
+    orc.scaler_update(st, A)
+    assert st.scale == f32(A) / f32(448.0)
+    for t in range(1, 60):
+        orc.scaler_update(st, 0.0)
+        e = f32(A * 2.0 ** -t)
+        assert st.ema == A * 2.0 ** -t
+        assert st.scale == max(e, f32(orc.EPS)) / f32(448.0), t
+    cur = orc.scaler_new(1, E5, stat=orc.STAT_EMA, alpha=1.0)
+    rng = np.random.default_rng(8)
+    for a in rng.random(30) * 1e4:
+        orc.scaler_update(cur, a)
+        assert cur.scale == orc.scale(a, E5)
+    k = orc.scaler_new(16, E4, stat=orc.STAT_EMA, alpha=0.01, margin=1.1)
+    for t in range(40):
+        assert k.scale == (1.0 if t < 16 else f32(f32(f32(7.25) * f32(1.1)) / f32(448.0)))
+        orc.scaler_update(k, 7.25)
+    with pytest.raises(ValueError):
+        orc.scaler_new(4, E4, stat=orc.STAT_EMA, alpha=0.0)
+
+
+def test_scaler_ema_moves_toward_new_values(orc):
+    """Between the old EMA and the new amax, never past either, and within
+    one fp64 rounding step of alpha*a + (1-alpha)*e computed exactly."""
+    rng = np.random.default_rng(9)
+    st = orc.scaler_new(1, E4, stat=orc.STAT_EMA, alpha=0.125)
+    prev = None
+    for a in (rng.random(200) * 100).astype(np.float32):
+        orc.scaler_update(st, float(a))
+        if prev is not None:
+            lo, hi = min(prev, float(a)), max(prev, float(a))
+            assert lo <= st.ema <= hi
+            exact = Fraction(0.125) * Fraction(float(a)) + Fraction(0.875) * Fraction(prev)
+            assert abs(Fraction(st.ema) - exact) <= abs(exact) * Fraction(1, 2 ** 51)
+        prev = st.ema
+
+
 # ------------------------------------------------------------------ GEMM
 def _rand_codes(rng, shape, fmt, lim=None):
     t_ok = {E4: [c for c in range(256) if c not in (0x7F, 0xFF)],
