@@ -196,11 +196,18 @@ def run_gpu(steps: int, warmup: int):
     am_tmp = torch.zeros(1, dtype=torch.float32, device=dev)
     st_tmp = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
     fq.fp8q_delayed_scaler_init(st_tmp, WINDOW, 448.0, 1e-12, 1.0)
+    # the other window statistics, at the longest window
+    st_mean = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
+    fq.fp8q_delayed_scaler_init_stat(st_mean, 1024, 448.0, 1e-12, 1.0, fq.STAT_MEAN)
+    st_ema = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
+    fq.fp8q_delayed_scaler_init_stat(st_ema, 1024, 448.0, 1e-12, 1.0, fq.STAT_EMA, 0.01)
     per = {
         "quantize_tensor_x": per_launch(lambda r: fq.fp8q_quantize_tensor(xs[r % N_ROT], n, fq.E4M3FN, sc_x, qx, am_tmp), 16),
         "quantize_tensor_g": per_launch(lambda r: fq.fp8q_quantize_tensor(gs[r % N_ROT], n, fq.E5M2, sc_g, qg, am_tmp), 16),
         "dequantize_x": per_launch(lambda r: fq.fp8q_dequantize(qx, fq.E4M3FN, 1, n, n, sc_x, fq.GRAN_TENSOR, 1, xhat, n), 16),
         "scaler_update": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_tmp, am_tmp), 16),
+        "scaler_update_mean_1024": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_mean, am_tmp), 16),
+        "scaler_update_ema_1024": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_ema, am_tmp), 16),
         "quantize_1x128": per_launch(lambda r: fq.fp8q_quantize_1x128(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, 1e-12, qX, LK,
                                                                        sX, LK // 128), 8),
         "gemm": per_launch(lambda r: fq.fp8q_gemm_blockscaled(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW,
@@ -425,6 +432,9 @@ def main():
             "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
                                 "frac_hbm": round(dq / HBM_PEAK_GBPS, 4)},
             "scaler_update": {"ms": round(per["scaler_update"], 4)},
+            "scaler_update_mean_1024": {"ms": round(per["scaler_update_mean_1024"], 4),
+                                        "note": "window mean over 1024 slots (fp64 pairwise)"},
+            "scaler_update_ema_1024": {"ms": round(per["scaler_update_ema_1024"], 4), "note": "EMA, alpha 0.01"},
             "quantize_1x128_t_bf16_16384x4096": {
                 "ms": round(per["quantize_1x128_t"], 4),
                 "GB/s": round(gbps(16384 * 4096 * (3 + 4 / 128), per["quantize_1x128_t"]), 1),

@@ -36,6 +36,7 @@ SYMBOLS = (
     "fp8q_quantize_mx",
     "fp8q_dequantize_mx",
     "fp8q_delayed_scaler_init",
+    "fp8q_delayed_scaler_init_stat",
     "fp8q_delayed_scaler_update",
     "fp8q_dequantize",
     "fp8q_gemm_blockscaled",
@@ -55,7 +56,11 @@ class Scaler(ctypes.Structure):
 
     _fields_ = [("ring", ctypes.c_float * 1024), ("window", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("pos", ctypes.c_int32), ("max_val", ctypes.c_float), ("eps", ctypes.c_float),
-                ("margin", ctypes.c_float), ("scale", ctypes.c_float)]
+                ("margin", ctypes.c_float), ("scale", ctypes.c_float), ("stat", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("reserved", ctypes.c_int32), ("ema", ctypes.c_double)]
+
+
+STAT_MAX, STAT_MEAN, STAT_EMA = 0, 1, 2
 
 
 SCALER_BYTES = ctypes.sizeof(Scaler)
@@ -85,6 +90,7 @@ def lib() -> ctypes.CDLL:
             "fp8q_quantize_mx": (i32, [vp, i32, i64, i64, i64, i32, vp, i64, vp, i64, vp]),
             "fp8q_dequantize_mx": (i32, [vp, i32, i64, i64, i64, vp, i64, vp, i32, i64, vp]),
             "fp8q_delayed_scaler_init": (i32, [vp, i32, f32, f32, f32, vp]),
+            "fp8q_delayed_scaler_init_stat": (i32, [vp, i32, f32, f32, f32, i32, f32, vp]),
             "fp8q_delayed_scaler_update": (i32, [vp, vp, vp]),
             "fp8q_dequantize": (i32, [vp, i32, i64, i64, i64, vp, i32, i64, vp, i32, i64, vp]),
             "fp8q_gemm_blockscaled": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64,
@@ -175,6 +181,11 @@ def fp8q_dequantize_mx(q, f, rows, cols, ldq, scales, ld_s, y, ldy, stream=None)
 
 def fp8q_delayed_scaler_init(state, window, max_val, eps, margin, stream=None) -> None:
     _check(lib().fp8q_delayed_scaler_init(_ptr(state), window, max_val, eps, margin, _stream(stream, state)))
+
+
+def fp8q_delayed_scaler_init_stat(state, window, max_val, eps, margin, stat, alpha=0.0, stream=None) -> None:
+    _check(lib().fp8q_delayed_scaler_init_stat(_ptr(state), window, max_val, eps, margin, stat, alpha,
+                                               _stream(stream, state)))
 
 
 def fp8q_delayed_scaler_update(state, amax, stream=None) -> None:

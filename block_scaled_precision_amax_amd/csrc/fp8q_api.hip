@@ -174,21 +174,31 @@ int fp8q_quantize_128x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t co
   return launch_quantize_128x128(x, dt, rows, cols, ldx, f, eps, q, ldq, scales, ld_s, S(stream));
 }
 
-int fp8q_delayed_scaler_init(fp8q_scaler* state, int32_t window, float max_val, float eps,
-                             float margin, void* stream) {
+int fp8q_delayed_scaler_init_stat(fp8q_scaler* state, int32_t window, float max_val, float eps, float margin,
+                                  fp8q_window_stat stat, float alpha, void* stream) {
   if (!state) return fail(FP8Q_EINVAL, "delayed_scaler_init: null pointer");
   if (window < 1 || window > 1024) return fail(FP8Q_EINVAL, "delayed_scaler_init: window must be in [1, 1024]");
   if (!(max_val > 0.0f) || !isfinite(max_val) || !(eps > 0.0f) || !isfinite(eps) ||
       !(margin > 0.0f) || !isfinite(margin))
     return fail(FP8Q_EINVAL, "delayed_scaler_init: max_val, eps and margin must be finite and > 0");
-  if (!aligned(state, 4)) return fail(FP8Q_EALIGN, "delayed_scaler_init: state must be 4-byte aligned");
-  return launch_scaler_init(state, window, max_val, eps, margin, S(stream));
+  if (stat != FP8Q_STAT_MAX && stat != FP8Q_STAT_MEAN && stat != FP8Q_STAT_EMA)
+    return fail(FP8Q_EINVAL, "delayed_scaler_init: unknown window statistic %d", (int)stat);
+  if (stat == FP8Q_STAT_EMA && !(alpha > 0.0f && alpha <= 1.0f))
+    return fail(FP8Q_EINVAL, "delayed_scaler_init: the EMA coefficient must be in (0, 1]");
+  if (!aligned(state, 8)) return fail(FP8Q_EALIGN, "delayed_scaler_init: state must be 8-byte aligned");
+  return launch_scaler_init(state, window, max_val, eps, margin, (int32_t)stat,
+                            stat == FP8Q_STAT_EMA ? alpha : 0.0f, S(stream));
+}
+
+int fp8q_delayed_scaler_init(fp8q_scaler* state, int32_t window, float max_val, float eps,
+                             float margin, void* stream) {
+  return fp8q_delayed_scaler_init_stat(state, window, max_val, eps, margin, FP8Q_STAT_MAX, 0.0f, stream);
 }
 
 int fp8q_delayed_scaler_update(fp8q_scaler* state, float* amax, void* stream) {
   if (!state || !amax) return fail(FP8Q_EINVAL, "delayed_scaler_update: null pointer");
-  if (!aligned(state, 4) || !aligned(amax, 4))
-    return fail(FP8Q_EALIGN, "delayed_scaler_update: state and amax must be 4-byte aligned");
+  if (!aligned(state, 8) || !aligned(amax, 4))
+    return fail(FP8Q_EALIGN, "delayed_scaler_update: state must be 8-byte and amax 4-byte aligned");
   return launch_scaler_update(state, amax, S(stream));
 }
 

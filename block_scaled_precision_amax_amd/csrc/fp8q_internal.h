@@ -148,8 +148,8 @@ int launch_dequantize_mx(const uint8_t* q, int fmt, int64_t rows, int64_t cols, 
 int launch_quantize_128x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                             float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                             hipStream_t st);
-int launch_scaler_init(fp8q_scaler* st_dev, int32_t window, float max_val, float eps, float margin,
-                       hipStream_t st);
+int launch_scaler_init(fp8q_scaler* st_dev, int32_t window, float max_val, float eps, float margin, int32_t stat,
+                       float alpha, hipStream_t st);
 int launch_scaler_update(fp8q_scaler* st_dev, float* amax, hipStream_t st);
 int launch_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64_t ldq,
                       const float* scales, int gran, int64_t ld_s, void* y, int out_dt, int64_t ldy,

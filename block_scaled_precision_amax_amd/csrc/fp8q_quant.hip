@@ -512,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_128x128(const void* __restri
 
 // ---------------------------------------------------------------- scaler
 __global__ void k_scaler_init(fp8q_scaler* st, int32_t window, float max_val, float eps,
-                              float margin) {
+                              float margin, int32_t stat, float alpha) {
   for (int i = threadIdx.x; i < 1024; i += blockDim.x) st->ring[i] = 0.0f;
   if (threadIdx.x == 0) {
     st->window = window;
@@ -522,6 +522,10 @@ __global__ void k_scaler_init(fp8q_scaler* st, int32_t window, float max_val, fl
     st->eps = eps;
     st->margin = margin;
     st->scale = 1.0f;
+    st->stat = stat;
+    st->alpha = alpha;
+    st->reserved = 0;
+    st->ema = 0.0;
   }
 }
 
@@ -536,28 +540,63 @@ __device__ __forceinline__ uint32_t hist_bits(float f) {
   return f > 0.0f ? __float_as_uint(f) : 0u;
 }
 
+// Window mean: lane l holds slots 16l .. 16l+15 (the new value in slot
+// pos, zeros past the window), sums them pairwise, and the butterfly over
+// lanes continues the same binary tree up to all 1024 slots (fp64 addition
+// is commutative, so both lanes of a pair form the same sum).
+__device__ double window_mean(const fp8q_scaler* st, int lane, int32_t window, int32_t pos, float a) {
+  double v[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = 16 * lane + k;
+    v[k] = i < window ? (double)(i == pos ? a : st->ring[i]) : 0.0;
+  }
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int k = 0; k < w; ++k) v[k] = __dadd_rn(v[2 * k], v[2 * k + 1]);
+  double s = v[0];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) s = __dadd_rn(s, __shfl_xor(s, o));
+  return s / (double)window;
+}
+
 __global__ __launch_bounds__(64) void k_scaler_update(fp8q_scaler* st, uint32_t* amax) {
   const int lane = threadIdx.x;
   float a = __uint_as_float(*amax);
   if (a != a) a = __uint_as_float(0x7FC00000u);
-  const int32_t window = st->window, pos = st->pos;
+  const int32_t window = st->window, pos = st->pos, stat = st->stat;
   int32_t count = st->count;
+  double ema = st->ema;
   __syncthreads();
+  if (stat == FP8Q_STAT_EMA) {
+    // e = alpha*a + (1-alpha)*e, two rounded products and a rounded sum
+    const double al = (double)st->alpha;
+    ema = count == 0 ? (double)a : __dadd_rn(__dmul_rn(al, (double)a), __dmul_rn(1.0 - al, ema));
+  }
   if (lane == 0) {
     *amax = 0u;  // consumed: ready to accumulate the next step
     st->ring[pos] = a;
     st->pos = pos + 1 == window ? 0 : pos + 1;
     st->count = count < window ? count + 1 : count;
+    if (stat == FP8Q_STAT_EMA) st->ema = ema;
   }
   count = count < window ? count + 1 : count;
   __syncthreads();
   if (count >= window) {
-    uint32_t m = 0;
-    for (int i = lane; i < window; i += 64) m = max(m, hist_bits(i == pos ? a : st->ring[i]));
-    m = wave_max(m);
+    float stat_v;
+    if (stat == FP8Q_STAT_MEAN) {
+      stat_v = (float)window_mean(st, lane, window, pos, a);
+    } else if (stat == FP8Q_STAT_EMA) {
+      stat_v = (float)ema;
+    } else {
+      uint32_t m = 0;
+      for (int i = lane; i < window; i += 64) m = max(m, hist_bits(i == pos ? a : st->ring[i]));
+      stat_v = __uint_as_float(wave_max(m));
+    }
     if (lane == 0) {
-      const float wmax = __uint_as_float(m);
-      const float mm = (wmax < st->eps) ? st->eps : wmax;  // NaN stays NaN
+      if (stat_v != stat_v) stat_v = __uint_as_float(0x7FC00000u);
+      const float mm = (stat_v < st->eps) ? st->eps : stat_v;  // NaN stays NaN
       const float t = mm * st->margin;
       st->scale = t / st->max_val;
     }
@@ -876,9 +915,9 @@ int launch_quantize_128x128(const void* x, int dt, int64_t rows, int64_t cols, i
   return check_launch("quantize_128x128");
 }
 
-int launch_scaler_init(fp8q_scaler* s, int32_t window, float max_val, float eps, float margin,
-                       hipStream_t st) {
-  hipLaunchKernelGGL(k_scaler_init, dim3(1), dim3(256), 0, st, s, window, max_val, eps, margin);
+int launch_scaler_init(fp8q_scaler* s, int32_t window, float max_val, float eps, float margin, int32_t stat,
+                       float alpha, hipStream_t st) {
+  hipLaunchKernelGGL(k_scaler_init, dim3(1), dim3(256), 0, st, s, window, max_val, eps, margin, stat, alpha);
   return check_launch("delayed_scaler_init");
 }
 

@@ -55,12 +55,19 @@ typedef enum { FP8Q_F32 = 0, FP8Q_BF16 = 1 } fp8q_dtype;
 typedef enum { FP8Q_E4M3FN = 0, FP8Q_E5M2 = 1 } fp8q_format;
 typedef enum { FP8Q_GRAN_TENSOR = 0, FP8Q_GRAN_1x128 = 1, FP8Q_GRAN_128x128 = 2 } fp8q_gran;
 
+/* Statistic of the amax history that sets the delayed scale ([A] 4.2: the
+ * window maximum; the mean as a gentler choice; an exponential moving
+ * average smoothing the amax, as Transformer Engine does; [A] 4.3). */
+typedef enum { FP8Q_STAT_MAX = 0, FP8Q_STAT_MEAN = 1, FP8Q_STAT_EMA = 2 } fp8q_window_stat;
+
 /* Delayed-scaling state ([A] 4.2 DelayedScaler): a window of the last
  * `window` amax values and the scale derived from them.  Device-resident,
- * caller-allocated, plain data (copy it to the host to checkpoint it).
- * `ring` holds the history (first `window` entries used), `pos` the next
- * slot, `count` the number of values seen (saturating at window), and
- * `scale` the dequantization scale in force, 1.0 until the window fills. */
+ * caller-allocated (8-byte aligned), plain data (copy it to the host to
+ * checkpoint it).  `ring` holds the history (first `window` entries used),
+ * `pos` the next slot, `count` the number of values seen (saturating at
+ * window), `scale` the dequantization scale in force, 1.0 until the window
+ * fills; `stat` the fp8q_window_stat, `alpha` the EMA coefficient and `ema`
+ * the EMA of every amax seen (fp64; 0 unless stat is FP8Q_STAT_EMA). */
 typedef struct {
   float ring[1024];
   int32_t window;
@@ -70,6 +77,10 @@ typedef struct {
   float eps;
   float margin;
   float scale;
+  int32_t stat;
+  float alpha;
+  int32_t reserved;
+  double ema;
 } fp8q_scaler;
 
 /* Library version (major*100 + minor). */
@@ -161,16 +172,31 @@ int fp8q_quantize_128x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t co
                           int64_t ld_s, void* stream);
 
 /* Set a device-resident scaler to its initial state ([A] 4.2 __init__):
- * empty history, scale = 1.0.  window in [1, 1024] (1 gives current
- * scaling), max_val > 0 (448 or 57344), eps > 0, margin > 0 ([A] 4.3;
- * 1.0 means none). */
+ * empty history, scale = 1.0, statistic the window maximum.  window in
+ * [1, 1024] (1 gives current scaling), max_val > 0 (448 or 57344),
+ * eps > 0, margin > 0 ([A] 4.3; 1.0 means none). */
 int fp8q_delayed_scaler_init(fp8q_scaler* state, int32_t window, float max_val, float eps,
                              float margin, void* stream);
 
-/* One delayed-scaling step ([A] 4.2 update): push *amax into the ring;
- * once `window` values have been seen, scale = fl32(fl32(max(max(ring),
- * eps) * margin) / max_val), otherwise the scale stays at its previous
- * value.  *amax is then reset to 0 so it can accumulate the next step
+/* As fp8q_delayed_scaler_init with the history statistic chosen ([A] 4.2,
+ * 4.3).  FP8Q_STAT_MAX: max of the window.  FP8Q_STAT_MEAN: mean of the
+ * window, its values summed in fp64 by pairwise (binary-tree) summation
+ * over the 1024 slots (unused slots 0), divided by window in fp64,
+ * rounded to fp32.  FP8Q_STAT_EMA: e = amax for the first value, then
+ * e = alpha*amax + (1-alpha)*e with each product and the sum rounded to
+ * fp64 (no fused multiply-add); alpha in (0, 1]; the statistic is fl32(e)
+ * and the window only sets when the scale first moves.  The scale is then
+ * fl32(fl32(max(stat, eps) * margin) / max_val).  A NaN amax makes max and
+ * mean NaN while it is in the window and the EMA NaN until re-init.
+ * Errors: FP8Q_EINVAL for a bad stat or alpha, as above otherwise. */
+int fp8q_delayed_scaler_init_stat(fp8q_scaler* state, int32_t window, float max_val, float eps,
+                                  float margin, fp8q_window_stat stat, float alpha, void* stream);
+
+/* One delayed-scaling step ([A] 4.2 update): push *amax into the ring
+ * (and into the EMA); once `window` values have been seen, scale =
+ * fl32(fl32(max(stat, eps) * margin) / max_val) with stat the state's
+ * statistic (max(ring) by default), otherwise the scale stays at its
+ * previous value.  *amax is then reset to 0 so it can accumulate the next step
  * (see fp8q_quantize_tensor).  A NaN amax propagates into the scale.
  * Runs as one wavefront; never syncs with the host. */
 int fp8q_delayed_scaler_update(fp8q_scaler* state, float* amax, void* stream);

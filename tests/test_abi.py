@@ -44,13 +44,26 @@ def test_version_and_status_strings(fq):
 
 
 def test_scaler_struct_layout(fq):
-    assert fq.SCALER_BYTES == 1024 * 4 + 7 * 4
+    assert fq.SCALER_BYTES == 1024 * 4 + 10 * 4 + 8
     assert fq.SCALER_SCALE_OFFSET == 1024 * 4 + 6 * 4
+    assert fq.Scaler.ema.offset % 8 == 0
 
 
 def _rc(fq, name, *args):
     rc = getattr(fq.lib(), name)(*args)
     return rc, fq.lib().fp8q_last_error().decode()
+
+
+def test_scaler_init_stat_validation(fq):
+    L = fq.lib()
+    f = ctypes.c_float
+    assert _rc(fq, "fp8q_delayed_scaler_init_stat", FAKE, 16, f(448.0), f(1e-12), f(1.0), 3, f(0.0), None)[0] == fq.EINVAL
+    assert _rc(fq, "fp8q_delayed_scaler_init_stat", FAKE, 16, f(448.0), f(1e-12), f(1.0), 2, f(0.0), None)[0] == fq.EINVAL
+    assert _rc(fq, "fp8q_delayed_scaler_init_stat", FAKE, 16, f(448.0), f(1e-12), f(1.0), 2, f(1.5), None)[0] == fq.EINVAL
+    assert _rc(fq, "fp8q_delayed_scaler_init_stat", FAKE, 0, f(448.0), f(1e-12), f(1.0), 1, f(0.0), None)[0] == fq.EINVAL
+    assert _rc(fq, "fp8q_delayed_scaler_init_stat", FAKE + 4, 16, f(448.0), f(1e-12), f(1.0), 1, f(0.0),
+               None)[0] == fq.EALIGN
+    assert L.fp8q_delayed_scaler_update(FAKE + 4, FAKE, None) == fq.EALIGN
 
 
 def test_amax_validation(fq):

@@ -439,11 +439,13 @@ def read_scaler(fq, st_dev):
 
 
 def assert_scaler_equal(g, o):
-    assert g.window == o.window and g.count == o.count and g.pos == o.pos
+    assert g.window == o.window and g.count == o.count and g.pos == o.pos and g.stat == o.stat
     assert np.array_equal(f32bits(np.array(g.ring[:g.window])), f32bits(np.array(o.ring[:o.window])))
     assert f32bits([g.scale])[0] == f32bits([o.scale])[0], (g.scale, o.scale)
-    for f in ("max_val", "eps", "margin"):
+    for f in ("max_val", "eps", "margin", "alpha"):
         assert f32bits([getattr(g, f)])[0] == f32bits([getattr(o, f)])[0]
+    ge, oe = np.array([g.ema], np.float64).view(np.uint64)[0], np.array([o.ema], np.float64).view(np.uint64)[0]
+    assert ge == oe or (np.isnan(g.ema) and np.isnan(o.ema)), (g.ema, o.ema)
 
 
 @pytest.mark.parametrize("window,fmt,margin", [(16, E4, 1.0), (1, E4, 1.0), (5, E5, 1.1), (1024, E5, 1.0)])
@@ -461,6 +463,45 @@ def test_scaler_sequence(fq, orc, gpu, window, fmt, margin):
         orc.scaler_update(o, float(a))
         torch.cuda.synchronize()
         assert amax.item() == 0.0
+        assert_scaler_equal(read_scaler(fq, st), o)
+
+
+@pytest.mark.parametrize("window,fmt,margin,stat,alpha", [(16, E4, 1.0, 1, 0.0), (1024, E5, 1.1, 1, 0.0),
+                                                         (37, E4, 1.0, 1, 0.0), (1, E5, 1.0, 1, 0.0),
+                                                         (16, E4, 1.0, 2, 0.01), (1, E5, 1.1, 2, 1.0),
+                                                         (1024, E4, 1.0, 2, 0.001), (5, E5, 1.0, 2, 0.3)])
+def test_scaler_statistics_sequence(fq, orc, gpu, window, fmt, margin, stat, alpha):
+    """Window mean (fp64 pairwise) and EMA (fp64 recurrence) scalers: state,
+    EMA bits and scale identical to the oracle's after every step, over a
+    ramp, a spike, zeros and random magnitudes spanning 30 octaves."""
+    st = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=gpu)
+    amax = torch.zeros(1, dtype=torch.float32, device=gpu)
+    fq.fp8q_delayed_scaler_init_stat(st, window, MAXF[fmt], EPS, margin, stat, alpha)
+    o = orc.scaler_new(window, fmt, EPS, margin, stat=stat, alpha=alpha)
+    rng = np.random.default_rng(window + 7 * stat)
+    seq = list((np.arange(1, 41) * 0.5).astype(np.float32)) + [np.float32(1e5), np.float32(0.0)]
+    seq += list(np.exp2(rng.uniform(-15, 15, size=window + 20)).astype(np.float32)) + [np.float32(0.0)] * 3
+    check_every = 1 if window < 64 else 17
+    for t, a in enumerate(seq):
+        amax.fill_(float(a))
+        fq.fp8q_delayed_scaler_update(st, amax)
+        orc.scaler_update(o, float(a))
+        if t % check_every == 0 or t == len(seq) - 1:
+            torch.cuda.synchronize()
+            assert_scaler_equal(read_scaler(fq, st), o)
+
+
+@pytest.mark.parametrize("stat,alpha", [(1, 0.0), (2, 0.25)])
+def test_scaler_statistics_nan(fq, orc, gpu, stat, alpha):
+    st = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=gpu)
+    amax = torch.zeros(1, dtype=torch.float32, device=gpu)
+    fq.fp8q_delayed_scaler_init_stat(st, 3, 448.0, EPS, 1.0, stat, alpha)
+    o = orc.scaler_new(3, E4, stat=stat, alpha=alpha)
+    for a in [1.0, 2.0, float("nan"), 3.0, 4.0, 5.0, 6.0]:
+        amax.fill_(a)
+        fq.fp8q_delayed_scaler_update(st, amax)
+        orc.scaler_update(o, a)
+        torch.cuda.synchronize()
         assert_scaler_equal(read_scaler(fq, st), o)
 
 
