@@ -236,6 +236,17 @@ def gemm_blockscaled(A: np.ndarray, fa: int, sA: np.ndarray, B: np.ndarray, fb: 
 
 
 # ---------------------------------------------------------------- MX (microscaling) FP8
+def gemm_blockscaled_q(A: np.ndarray, fa: int, sA: np.ndarray, B: np.ndarray, fb: int, sB: np.ndarray, gb: int,
+                       fc: int, eps: float = EPS, rows: np.ndarray | None = None):
+    """The GEMM's output quantized 1x128 for the next layer: C = fl32 of the
+    exact block-scaled product (gemm_blockscaled), then quantize_blocks(C, 1,
+    128, fc, eps).  Returns (codes [rows, N], scales [rows, N/128], C fp32)."""
+    C, _ = gemm_blockscaled(A, fa, sA, B, fb, sB, gb, rows=rows)
+    C32 = C.astype(np.float32)  # round to nearest even
+    q, s = quantize_blocks(C32, 1, 128, fc, eps)
+    return q, s, C32
+
+
 def quantize_mx(x: np.ndarray, fmt: int):
     """32-element blocks along rows with power-of-two E8M0 scales (OCP MX v1.0, 6.3).
     Returns (codes [rows, cols], scale bytes [rows, cols/32])."""

@@ -704,3 +704,58 @@ def test_gemm_mx_unit_scales_is_integer_matmul(orc):
     B = np.vectorize(code.get)(Bi).astype(np.uint8)
     C, _ = orc.gemm_mx(A, E4, np.full((8, 3), 127, np.uint8), B, E4, np.full((40, 3), 127, np.uint8))
     assert np.array_equal(C, (Ai @ Bi.T).astype(np.float64))
+
+
+# ------------------------------------------------------------------ GEMM with quantized output
+def small_int_codes(orc, shape, rng, fmt):
+    """Codes whose values are the integers -4 .. 4 (exact in both formats)."""
+    vals = rng.integers(-4, 5, size=shape).astype(np.float32)
+    return orc.encode_array(vals, fmt).reshape(shape), vals
+
+
+def test_gemm_q_is_quantized_integer_matmul(orc):
+    """With small-integer codes and power-of-two scales every sum is exact, so
+    C equals an int64 matmul scaled by powers of two; the codes and scales
+    must be quantize_1x128 of that C, blocks running along N (128 columns
+    of one output row)."""
+    rng = np.random.default_rng(12)
+    M, N, K = 5, 256, 384
+    for fa, fb, fc in ((E4, E4, E4), (E5, E4, E5)):
+        A, av = small_int_codes(orc, (M, K), rng, fa)
+        B, bv = small_int_codes(orc, (N, K), rng, fb)
+        ea = rng.integers(-2, 3, size=(M, K // 128))
+        eb = rng.integers(-2, 3, size=(N // 128, K // 128))
+        sA = np.ldexp(np.float32(1), ea).astype(np.float32)
+        sB = np.ldexp(np.float32(1), eb).astype(np.float32)
+        C = np.zeros((M, N))
+        for kb in range(K // 128):
+            blk = av[:, 128 * kb:128 * kb + 128].astype(np.int64) @ bv[:, 128 * kb:128 * kb + 128].astype(np.int64).T
+            C += blk * np.ldexp(1.0, ea[:, kb])[:, None] * np.repeat(np.ldexp(1.0, eb[:, kb]), 128)[None, :]
+        q, s, C32 = orc.gemm_blockscaled_q(A, fa, sA, B, fb, sB, orc.GRAN_128x128, fc)
+        assert np.array_equal(C32, C.astype(np.float32))
+        for r in range(M):
+            for cb in range(N // 128):
+                amax = np.float32(np.abs(C[r, 128 * cb:128 * cb + 128]).max())
+                assert s[r, cb] == np.float32(max(amax, np.float32(orc.EPS)) / np.float32(orc.MAX_FINITE[fc]))
+        wq, _ = orc.quantize_blocks(C.astype(np.float32), 1, 128, fc)
+        assert np.array_equal(q, wq)
+
+
+def test_gemm_q_row_scale_closed_form(orc):
+    """One nonzero per A row picks out one B row, so C's row r is B's row
+    (r mod N) transposed; its 1x128 scales are fl32(amax / MAX) of those
+    128-column pieces and a column of zeros in a block leaves code 0."""
+    M, N, K = 3, 128, 128
+    A = np.zeros((M, K), np.uint8)
+    for r in range(M):
+        A[r, r] = 0x38  # 1.0
+    rng = np.random.default_rng(2)
+    B, bv = small_int_codes(orc, (N, K), rng, E4)
+    B[:, 0] = 0
+    bv[:, 0] = 0
+    q, s, C32 = orc.gemm_blockscaled_q(A, E4, np.ones((M, 1), np.float32), B, E4, np.ones((1, 1), np.float32),
+                                       orc.GRAN_128x128, E4)
+    for r in range(M):
+        assert np.array_equal(C32[r], bv[:, r])
+        assert s[r, 0] == np.float32(max(np.abs(bv[:, r]).max(), np.float32(orc.EPS))) / np.float32(448.0)
+    assert np.all(q[0] == 0)  # B[:, 0] is zero: row 0 of C is zero, code 0x00
