@@ -216,6 +216,13 @@ def run_gpu(steps: int, warmup: int):
                                                                         LK, sW, fq.GRAN_128x128, LK // 128, 1, C, LN, LM,
                                                                         LN, LK), 4),
     }
+    # the same GEMM with its output quantized 1x128 (E4M3FN) in the epilogue
+    qC = torch.empty(LM, LN, dtype=torch.uint8, device=dev)
+    sC = torch.empty(LM, LN // 128, dtype=torch.float32, device=dev)
+    per["gemm_q"] = per_launch(lambda r: fq.fp8q_gemm_blockscaled_q(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN,
+                                                                    LK, sW, fq.GRAN_128x128, LK // 128, 1, fq.E4M3FN,
+                                                                    1e-12, qC, LN, sC, LN // 128, LM, LN, LK), 4)
+    del qC, sC
     # The other GEMM shapes (per-kernel figures only, not part of the step):
     # 4096^3 with 1x128 A and 128x128 B scales, bf16 out; and the backward
     # GEMMs of a 4096-wide layer over 16384 tokens, fp32 out: dgrad (E5M2
@@ -382,6 +389,7 @@ def main():
 
     gemm_tflops = alg["gemm_flop"] / (per["gemm"] * 1e-3) / 1e12
     fast_tflops = alg["gemm_flop"] / (per["gemm_fast"] * 1e-3) / 1e12
+    q_tflops = alg["gemm_flop"] / (per["gemm_q"] * 1e-3) / 1e12
     q_t = gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_x"])
     q_g = gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_g"])
     q_1 = gbps(alg["quantize_1x128_bytes"], per["quantize_1x128"])
@@ -423,6 +431,9 @@ def main():
             "gemm_blockscaled_fast": {"ms": round(per["gemm_fast"], 4), "TFLOP/s": round(fast_tflops, 2),
                                       "frac_fp8_peak": round(fast_tflops / FP8_PEAK_TFLOPS, 4),
                                       "note": "FP8 MFMA path, measured outside the step"},
+            "gemm_blockscaled_q": {"ms": round(per["gemm_q"], 4), "TFLOP/s": round(q_tflops, 2),
+                                   "frac_bf16_peak": round(q_tflops / BF16_PEAK_TFLOPS, 4),
+                                   "note": "exact path, output quantized 1x128 to E4M3FN in the epilogue"},
             "quantize_1x128_bf16": {"ms": round(per["quantize_1x128"], 4), "GB/s": round(q_1, 1),
                                     "frac_hbm": round(q_1 / HBM_PEAK_GBPS, 4)},
             "quantize_tensor_bf16_e4m3": {"ms": round(per["quantize_tensor_x"], 4), "GB/s": round(q_t, 1),

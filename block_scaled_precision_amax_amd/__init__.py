@@ -42,6 +42,7 @@ SYMBOLS = (
     "fp8q_gemm_blockscaled",
     "fp8q_gemm_blockscaled_fast",
     "fp8q_gemm_mx",
+    "fp8q_gemm_blockscaled_q",
 )
 
 
@@ -98,6 +99,8 @@ def lib() -> ctypes.CDLL:
             "fp8q_gemm_blockscaled_fast": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64,
                                                  vp, i32, i64, i64, i64, i64, vp]),
             "fp8q_gemm_mx": (i32, [vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp, i32, i64, i64, i64, i64, vp]),
+            "fp8q_gemm_blockscaled_q": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64, i32, f32,
+                                              vp, i64, vp, i64, i64, i64, i64, vp]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -213,3 +216,10 @@ def fp8q_gemm_blockscaled_fast(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb
 def fp8q_gemm_mx(A, fa, lda, sA, ld_sa, B, fb, ldb, sB, ld_sb, C, ldc, M, N, K, stream=None) -> None:
     _check(lib().fp8q_gemm_mx(_ptr(A), fa, lda, _ptr(sA), ld_sa, _ptr(B), fb, ldb, _ptr(sB), ld_sb, _ptr(C), _dt(C),
                               ldc, M, N, K, _stream(stream, A)))
+
+
+def fp8q_gemm_blockscaled_q(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb, sB_sn, sB_skb, fc, eps, Cq, ldcq, Cs,
+                            ld_cs, M, N, K, stream=None) -> None:
+    _check(lib().fp8q_gemm_blockscaled_q(_ptr(A), fa, lda, _ptr(sA), sA_sm, sA_skb, _ptr(B), fb, ldb, _ptr(sB), gb,
+                                         sB_sn, sB_skb, fc, eps, _ptr(Cq), ldcq, _ptr(Cs), ld_cs, M, N, K,
+                                         _stream(stream, A)))

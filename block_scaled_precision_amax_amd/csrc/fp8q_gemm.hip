@@ -44,6 +44,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 static constexpr int BK = 128;
 static constexpr int kGemmThreads = 512;  // eight wavefronts, 2 x 4
+// Output kinds beside FP8Q_F32 / FP8Q_BF16: 1x128 FP8 codes of C (E4M3FN or
+// E5M2) with one fp32 scale per 128 columns of a row.
+static constexpr int kOutQ = 2;
 
 // Per path: wavefront grid (2 x 4) and MFMA tiles of 16x16 per wavefront.
 // FP8 path: 8 x 4 tiles (128 x 64 per wavefront, 256 x 256 per workgroup);
@@ -168,6 +171,68 @@ __device__ __forceinline__ void dma_tile(uint8_t* lds, const uint8_t* base, cons
     lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds + (wave * (R / 64) + u) * 1024)), base, off[u]);
 }
 
+// 1x128 quantization of C in the epilogue: the 128 columns of a row block
+// belong to two neighbouring wavefronts (wn = 2c, 2c+1; 64 columns each).
+// Each takes the maximum |C| of its part of every row over its four column
+// tiles and the 16 lanes of a DPP row, the two parts meet through LDS, and
+// each element is encoded with s = fl32(max(amax, eps) / MAX) exactly as
+// fp8q_quantize_1x128 encodes an fp32 input: the correctly rounded
+// quotient (Markstein's correction while s lies in [2^-80, 2^80], IEEE
+// division otherwise), saturated, rounded to nearest even, NaN -> 0x7F.
+// Columns past N count as 0 and are not stored.
+template <int QF, int TI, int TJ>
+__device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* lds_rmax, int wave, int lr, int lq,
+                                           int64_t row0, int64_t col0, int64_t M, int64_t N, float eps,
+                                           uint8_t* __restrict__ Cq, int64_t ldc, float* __restrict__ Cs,
+                                           int64_t ld_cs, bool writes_scale) {
+  uint32_t rm[TI][4];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+        if (col0 + 16 * j + lr < N) m = max(m, __float_as_uint(acc[i][j][e]) & 0x7FFFFFFFu);
+      rm[i][e] = row16_max(m);
+    }
+  // row 16i + 4lq + e of this wavefront's part; lane lr publishes the
+  // values with 4i + e = lr (mod 16)
+  uint32_t* mine = lds_rmax + wave * TI * 16;
+#pragma unroll
+  for (int k0 = 0; k0 < TI * 4; k0 += 16) {
+    uint32_t v = 0;
+#pragma unroll
+    for (int k = k0; k < k0 + 16 && k < TI * 4; ++k)
+      if (lr == k - k0) v = rm[k >> 2][k & 3];
+    const int k = k0 + lr;
+    if (k < TI * 4) mine[16 * (k >> 2) + 4 * lq + (k & 3)] = v;
+  }
+  __syncthreads();
+  const uint32_t* other = lds_rmax + (wave ^ 1) * TI * 16;
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rw = 16 * i + 4 * lq + e;
+      const int64_t row = row0 + rw;
+      const float amax = __uint_as_float(canon_abs_bits(max(rm[i][e], other[rw])));
+      const float s = block_scale<QF>(amax, eps);
+      if (row >= M) continue;
+      if (writes_scale && lr == 0 && col0 < N) Cs[row * ld_cs + (col0 >> 7)] = s;
+      const bool fast = scale_ok(s);
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int64_t col = col0 + 16 * j + lr;
+        if (col >= N) continue;
+        const float x = acc[i][j][e];
+        const uint32_t c = fast ? (cvt2<QF, false>(sat<QF>(div_rn(x, s, r)), 0.0f, 0u) & 0xFFu) : enc1<QF>(x / s);
+        Cq[row * ldc + col] = (uint8_t)c;
+      }
+    }
+}
+
 // One workgroup of eight wavefronts computes a BM x BN tile of C; wavefront
 // (wm, wn) = (w/4, w%4) owns TI x TJ MFMA tiles of 16x16 at rows
 // 16*TI*wm.. and columns 16*TJ*wn.. (64 columns: inside one 128-column
@@ -181,8 +246,8 @@ template <int FA, int FB, int GB, int ODT, bool FAST>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t sA_sm,
     int64_t sA_skb, const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
-    int64_t sB_sn, int64_t sB_skb, void* __restrict__ C, int64_t ldc, int64_t M, int64_t N,
-    int64_t K, int64_t ntm, int64_t ntn) {
+    int64_t sB_sn, int64_t sB_skb, void* __restrict__ C, int64_t ldc, float* __restrict__ Cs,
+    int64_t ld_cs, float qeps, int64_t M, int64_t N, int64_t K, int64_t ntm, int64_t ntn) {
   using G = Cfg<FAST>;
   constexpr int BM = G::BM, BN = G::BN, TI = G::TI, TJ = G::TJ, NST = G::NST;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[NST][BM * BK];
@@ -192,6 +257,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   constexpr bool SB_COLS = GB == FP8Q_GRAN_1x128;
   __shared__ __attribute__((aligned(16))) float lds_sb[NST][SB_COLS ? BN : 1];
   constexpr int NL = G::NLOAD + (SB_COLS ? 1 : 0);  // loads per wavefront per K block
+  // quantized output: each wavefront's row maxima, read by its neighbour
+  __shared__ uint32_t lds_rmax[ODT >= kOutQ ? 8 * TI * 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -430,6 +497,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   compute(kb, st);
 
   // ---- epilogue
+  if constexpr (ODT >= kOutQ) {
+    epilogue_q<ODT - kOutQ, TI, TJ>(acc, lds_rmax, wave, lr, lq, m0 + wm * TI * 16, wcol0, M, N, qeps,
+                                    (uint8_t*)C, ldc, Cs, ld_cs, (wn & 1) == 0);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int64_t col = wcol0 + 16 * j + lr;
@@ -605,11 +677,39 @@ int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int
 template <int FA, int FB, int GB, int ODT, bool FAST>
 static void launch_t(const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
                      const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn, int64_t sB_skb, void* C,
-                     int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                     int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st, float* Cs = nullptr,
+                     int64_t ld_cs = 0, float qeps = 0.0f) {
   constexpr int BM = Cfg<FAST>::BM, BN = Cfg<FAST>::BN;
   const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   hipLaunchKernelGGL((k_gemm<FA, FB, GB, ODT, FAST>), dim3((unsigned)(ntm * ntn)), dim3(kGemmThreads), 0, st, A,
-                     lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, M, N, K, ntm, ntn);
+                     lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, Cs, ld_cs, qeps, M, N, K, ntm,
+                     ntn);
+}
+
+template <int FA, int FB, int GB>
+static void launch_q_g(int fc, const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
+                       const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn, int64_t sB_skb, uint8_t* Cq,
+                       int64_t ldc, float* Cs, int64_t ld_cs, float eps, int64_t M, int64_t N, int64_t K,
+                       hipStream_t st) {
+  if (fc == FP8Q_E4M3FN)
+    launch_t<FA, FB, GB, kOutQ + FP8Q_E4M3FN, false>(A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc,
+                                                     M, N, K, st, Cs, ld_cs, eps);
+  else
+    launch_t<FA, FB, GB, kOutQ + FP8Q_E5M2, false>(A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc,
+                                                   M, N, K, st, Cs, ld_cs, eps);
+}
+
+template <int FA, int FB>
+static void launch_q_f(int gb, int fc, const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm,
+                       int64_t sA_skb, const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn,
+                       int64_t sB_skb, uint8_t* Cq, int64_t ldc, float* Cs, int64_t ld_cs, float eps, int64_t M,
+                       int64_t N, int64_t K, hipStream_t st) {
+  if (gb == FP8Q_GRAN_128x128)
+    launch_q_g<FA, FB, FP8Q_GRAN_128x128>(fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs,
+                                          ld_cs, eps, M, N, K, st);
+  else
+    launch_q_g<FA, FB, FP8Q_GRAN_1x128>(fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs,
+                                        ld_cs, eps, M, N, K, st);
 }
 
 template <int FA, int FB, int GB, bool FAST>
@@ -647,6 +747,26 @@ static void dispatch_f(int fa, int fb, int gb, int out_dt, const uint8_t* A, int
     dispatch_g<0, 1, FAST>(gb, out_dt, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, M, N, K, st);
   else
     dispatch_g<1, 1, FAST>(gb, out_dt, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, M, N, K, st);
+}
+
+int launch_gemm_q(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
+                  const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb, int64_t sB_sn, int64_t sB_skb,
+                  int fc, float eps, uint8_t* Cq, int64_t ldc, float* Cs, int64_t ld_cs, int64_t M, int64_t N,
+                  int64_t K, hipStream_t st) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "gemm_q: more than 2^31-1 output tiles");
+  if ((M - 1) * lda + K > 0xFFFFFFFFll || (N - 1) * ldb + K > 0xFFFFFFFFll ||
+      (gb == FP8Q_GRAN_1x128 && (N - 1) * sB_sn > 0x3FFFFFFFll))
+    return fail(FP8Q_ESHAPE, "gemm_q: an operand spans 4 GiB or more");
+  if (fa == FP8Q_E4M3FN && fb == FP8Q_E4M3FN)
+    launch_q_f<0, 0>(gb, fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs, ld_cs, eps, M, N, K, st);
+  else if (fa == FP8Q_E5M2 && fb == FP8Q_E4M3FN)
+    launch_q_f<1, 0>(gb, fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs, ld_cs, eps, M, N, K, st);
+  else if (fa == FP8Q_E4M3FN && fb == FP8Q_E5M2)
+    launch_q_f<0, 1>(gb, fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs, ld_cs, eps, M, N, K, st);
+  else
+    launch_q_f<1, 1>(gb, fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs, ld_cs, eps, M, N, K, st);
+  return check_launch("gemm_blockscaled_q");
 }
 
 int launch_gemm(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm,

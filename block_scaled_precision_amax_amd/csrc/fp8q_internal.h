@@ -159,6 +159,10 @@ int launch_gemm(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t 
                 int64_t sB_sn, int64_t sB_skb, void* C, int out_dt, int64_t ldc, int64_t M,
                 int64_t N, int64_t K, bool fast, hipStream_t st);
 
+int launch_gemm_q(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
+                  const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb, int64_t sB_sn, int64_t sB_skb,
+                  int fc, float eps, uint8_t* Cq, int64_t ldc, float* Cs, int64_t ld_cs, int64_t M, int64_t N,
+                  int64_t K, hipStream_t st);
 int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
                    int fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C, int out_dt, int64_t ldc,
                    int64_t M, int64_t N, int64_t K, hipStream_t st);

@@ -252,6 +252,22 @@ int fp8q_gemm_blockscaled_fast(const uint8_t* A, fp8q_format fa, int64_t lda, co
                                int64_t sB_skb, void* C, fp8q_dtype out_dt, int64_t ldc, int64_t M,
                                int64_t N, int64_t K, void* stream);
 
+/* fp8q_gemm_blockscaled with the output quantized in the epilogue, for
+ * the next layer's input ([A] 5.1: casts to and from a wide type between
+ * FP8 operations eat the gain; [H] fine-grained 1x128 scaling): the fp32
+ * C of fp8q_gemm_blockscaled is never written; instead, per row and 128
+ * consecutive columns, Cs[m*ld_cs + n/128] = fl32(max(amax, eps) / MAX_fc)
+ * and Cq[m*ldcq + n] = enc_fc(fl32(C[m,n] / s)), bit for bit what
+ * fp8q_quantize_1x128 makes of that fp32 C (saturating, RNE, NaN -> 0x7F).
+ * Arguments as fp8q_gemm_blockscaled (exact path) plus: fc the output
+ * format, eps > 0, Cq [M, N] codes with ldcq >= N, Cs [M, N/128] fp32 with
+ * ld_cs >= N/128.  N % 128 == 0 and K % 128 == 0 (else FP8Q_ESHAPE). */
+int fp8q_gemm_blockscaled_q(const uint8_t* A, fp8q_format fa, int64_t lda, const float* sA, int64_t sA_sm,
+                            int64_t sA_skb, const uint8_t* B, fp8q_format fb, int64_t ldb, const float* sB,
+                            fp8q_gran gb, int64_t sB_sn, int64_t sB_skb, fp8q_format fc, float eps, uint8_t* Cq,
+                            int64_t ldcq, float* Cs, int64_t ld_cs, int64_t M, int64_t N, int64_t K,
+                            void* stream);
+
 /* MX GEMM: C[m,n] = sum over 32-element K blocks kb of
  *   2^(sA[m,kb] - 127) * 2^(sB[n,kb] - 127) * sum_{k in kb} dec(A[m,k]) dec(B[n,k]),
  * the product of two fp8q_quantize_mx outputs (B as [N,K], K-contiguous).

@@ -227,3 +227,110 @@ def test_gemm_fast_4096_cubed_sampled(fq, orc, gpu):
     Cref, D = orc.gemm_blockscaled(qa.numpy(), E4, sa.numpy(), qb.numpy(), E4, sb.numpy(), G128, rows=rows)
     err = np.abs(C[rows].to(torch.float64).numpy() - Cref)
     assert np.all(err <= FAST_TOL * D)
+
+
+# ------------------------------------------------------------------ quantized output (epilogue)
+def run_gemm_q(fq, A, fa, sA, B, fb, sB, gb, fc, pad_q=0, pad_s=0, dev="cuda"):
+    M, K = A.shape
+    N = B.shape[0]
+    q = torch.full((M, N + pad_q), 0xAA, dtype=torch.uint8, device=dev)
+    s = torch.full((M, N // 128 + pad_s), -7.0, dtype=torch.float32, device=dev)
+    fq.fp8q_gemm_blockscaled_q(A.to(dev), fa, K, sA.to(dev), sA.shape[1], 1, B.to(dev), fb, K, sB.to(dev), gb,
+                               sB.shape[1], 1, fc, 1e-12, q, N + pad_q, s, N // 128 + pad_s, M, N, K)
+    torch.cuda.synchronize()
+    q, s = q.cpu(), s.cpu()
+    if pad_q:
+        assert torch.all(q[:, N:] == 0xAA), "wrote past the code row"
+    if pad_s:
+        assert torch.all(s[:, N // 128:] == -7.0), "wrote past the scale row"
+    return q[:, :N].numpy(), s[:, :N // 128].numpy()
+
+
+def int_codes(orc, shape, fmt, seed):
+    """Codes of the integers -4 .. 4: with power-of-two scales every sum the
+    kernel forms is exact, so its fp32 C equals fl32 of the exact product."""
+    rng = np.random.default_rng(seed)
+    v = rng.integers(-4, 5, size=shape).astype(np.float32)
+    return torch.from_numpy(orc.encode_array(v, fmt).reshape(shape))
+
+
+def pow2_scales(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.ldexp(torch.ones(shape), torch.randint(-2, 3, shape, generator=g)).to(torch.float32)
+
+
+@pytest.mark.parametrize("fa,fb,gb,fc", [(E4, E4, G128, E4), (E5, E4, G128, E5), (E4, E4, G1, E4),
+                                         (E5, E4, G1, E4), (E4, E5, G128, E5)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (1, 128, 128), (300, 640, 1024), (129, 256, 256)])
+def test_gemm_q_exact_inputs_match_oracle(fq, orc, gpu, fa, fb, gb, fc, M, N, K):
+    """Integer codes and power-of-two scales (exact sums): codes and scales
+    bit-identical to the oracle's quantize_1x128 of fl32(C_exact), over
+    ragged M, N = 128 (one block, half a tile) and N not a multiple of the
+    256-column tile."""
+    A = int_codes(orc, (M, K), fa, M + K)
+    B = int_codes(orc, (N, K), fb, N + K + 1)
+    sA = pow2_scales((M, K // 128), 3)
+    sB = pow2_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 4)
+    q, s = run_gemm_q(fq, A, fa, sA, B, fb, sB, gb, fc, pad_q=16, pad_s=2)
+    wq, ws, _ = orc.gemm_blockscaled_q(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb, fc)
+    assert np.array_equal(s.view(np.uint32), ws.view(np.uint32))
+    assert np.array_equal(q, wq)
+
+
+@pytest.mark.parametrize("fa,fb,gb,fc", [(E4, E4, G128, E4), (E5, E4, G1, E5)])
+def test_gemm_q_equals_gemm_then_quantize(fq, orc, gpu, fa, fb, gb, fc):
+    """Random codes over the whole code space and random scales: the fused
+    output is bit for bit fp8q_quantize_1x128 of fp8q_gemm_blockscaled's
+    fp32 C (the same accumulation, quantized in registers instead of after
+    a round trip through HBM)."""
+    M, N, K = 300, 640, 768
+    A = W.fp8_codes((M, K), fa, seed=71)
+    B = W.fp8_codes((N, K), fb, seed=72)
+    sA = rand_scales((M, K // 128), 73)
+    sB = rand_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 74)
+    q, s = run_gemm_q(fq, A, fa, sA, B, fb, sB, gb, fc)
+    C = run_gemm(fq, A, fa, sA, B, fb, sB, gb).to(gpu)
+    q2 = torch.empty(M, N, dtype=torch.uint8, device=gpu)
+    s2 = torch.empty(M, N // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_1x128(C, M, N, N, fc, 1e-12, q2, N, s2, N // 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(s.view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(q, q2.cpu().numpy())
+    # and against the oracle, through the error bound of the GEMM
+    Cref, D = orc.gemm_blockscaled(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb)
+    check(C.cpu(), Cref, D, "unfused C")
+
+
+def test_gemm_q_layer_sampled(fq, orc, gpu):
+    """The layer, 16384 x 18432 x 7168, output quantized 1x128 to E4M3FN:
+    on 16 sampled rows the scales lie within the GEMM's error bound of the
+    oracle's and every decoded output within FP8 rounding of the oracle's C."""
+    M, N, K = 16384, 18432, 7168
+    x = W.activation(M, K, seed=4, factor=1e3, dtype=torch.bfloat16, device=gpu)
+    w = W.weight(N, K, seed=40, device=gpu)
+    qa = torch.empty(M, K, dtype=torch.uint8, device=gpu)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=gpu)
+    qb = torch.empty(N, K, dtype=torch.uint8, device=gpu)
+    sb = torch.empty(N // 128, K // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_1x128(x, M, K, K, E4, 1e-12, qa, K, sa, K // 128)
+    fq.fp8q_quantize_128x128(w, N, K, K, E4, 1e-12, qb, K, sb, K // 128)
+    qc = torch.empty(M, N, dtype=torch.uint8, device=gpu)
+    sc = torch.empty(M, N // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_gemm_blockscaled_q(qa, E4, K, sa, K // 128, 1, qb, E4, K, sb, G128, K // 128, 1, E4, 1e-12, qc, N, sc,
+                               N // 128, M, N, K)
+    torch.cuda.synchronize()
+    rows = sampled_rows(M, 16)
+    ri = torch.from_numpy(rows).to(gpu)
+    Cref, D = orc.gemm_blockscaled(qa[ri].cpu().numpy(), E4, sa[ri].cpu().numpy(), qb.cpu().numpy(), E4,
+                                   sb.cpu().numpy(), G128)
+    q = qc[ri].cpu().numpy()
+    s = sc[ri].cpu().numpy().astype(np.float64)
+    dec = orc.decode_table(E4)[q].astype(np.float64)
+    Cb = np.abs(Cref).reshape(len(rows), N // 128, 128)
+    Db = D.reshape(len(rows), N // 128, 128)
+    s_ref = Cb.max(axis=2) / 448.0
+    # amax moves by at most the largest error bound in its block
+    assert np.all(np.abs(s - s_ref) <= (TOL * Db.max(axis=2)) / 448.0 + 2.0 ** -23 * s_ref)
+    y = (dec.reshape(len(rows), N // 128, 128) * s[:, :, None]).reshape(len(rows), N)
+    bound = 2.0 ** -4 * np.abs(Cref) + 2.0 ** -10 * np.repeat(s, 128, axis=1) + 2 * TOL * D
+    assert np.all(np.abs(y - Cref) <= bound)
