@@ -170,3 +170,56 @@ def test_gemm_validation(fq):
     assert call(sA_sm=-1)[0] == fq.EINVAL
     assert call(A=FAKE + 8)[0] == fq.EALIGN
     assert call(ldb=264)[0] == fq.EALIGN
+
+
+def test_mx_validation(fq):
+    q = "fp8q_quantize_mx"
+    assert _rc(fq, q, None, 1, 4, 256, 256, 0, FAKE, 256, FAKE, 8, None)[0] == fq.EINVAL
+    assert _rc(fq, q, FAKE, 1, 4, 256, 256, 2, FAKE, 256, FAKE, 8, None)[0] == fq.EINVAL  # format
+    rc, msg = _rc(fq, q, FAKE, 1, 4, 240, 256, 0, FAKE, 256, FAKE, 8, None)
+    assert rc == fq.ESHAPE and "multiple of 32" in msg
+    assert _rc(fq, q, FAKE, 1, 4, 256, 256, 0, FAKE, 256, FAKE, 7, None)[0] == fq.EINVAL  # ld_s
+    assert _rc(fq, q, FAKE, 1, 4, 256, 260, 0, FAKE, 256, FAKE, 8, None)[0] == fq.EALIGN  # bf16 rows
+    assert _rc(fq, q, FAKE, 1, 4, 256, 256, 0, FAKE + 8, 256, FAKE, 8, None)[0] == fq.EALIGN
+    d = "fp8q_dequantize_mx"
+    assert _rc(fq, d, FAKE, 0, 4, 256, 256, None, 8, FAKE, 1, 256, None)[0] == fq.EINVAL
+    assert _rc(fq, d, FAKE, 0, 4, 96 + 4, 256, FAKE, 8, FAKE, 1, 256, None)[0] == fq.ESHAPE
+    assert _rc(fq, d, FAKE, 0, 4, 256, 260, FAKE, 8, FAKE, 1, 256, None)[0] == fq.EALIGN  # ldq % 8
+    assert _rc(fq, d, FAKE, 0, 4, 256, 256, FAKE, 8, FAKE, 1, 260, None)[0] == fq.EALIGN  # bf16 rows
+    g = "fp8q_gemm_mx"
+    okg = dict(A=FAKE, fa=0, lda=256, sA=FAKE, ld_sa=8, B=FAKE, fb=0, ldb=256, sB=FAKE, ld_sb=8, C=FAKE, odt=0,
+               ldc=128, M=64, N=128, K=256)
+
+    def call(**kw):
+        a = {**okg, **kw}
+        return _rc(fq, g, a["A"], a["fa"], a["lda"], a["sA"], a["ld_sa"], a["B"], a["fb"], a["ldb"], a["sB"],
+                   a["ld_sb"], a["C"], a["odt"], a["ldc"], a["M"], a["N"], a["K"], None)
+
+    assert call(sB=None)[0] == fq.EINVAL
+    assert call(fb=5)[0] == fq.EINVAL
+    rc, msg = call(K=224, lda=224, ldb=224, ld_sa=8, ld_sb=8)
+    assert rc == fq.ESHAPE and "multiple of 128" in msg
+    assert call(ld_sa=4)[0] == fq.EINVAL
+    assert call(ld_sb=10)[0] == fq.EALIGN
+    assert call(lda=264)[0] == fq.EALIGN
+    assert call(sA=FAKE + 2)[0] == fq.EALIGN
+
+
+def test_gemm_q_validation(fq):
+    ok = dict(A=FAKE, fa=0, lda=256, sA=FAKE, sA_sm=2, sA_skb=1, B=FAKE, fb=0, ldb=256, sB=FAKE, gb=2,
+              sB_sn=2, sB_skb=1, fc=0, eps=1e-12, Cq=FAKE, ldcq=256, Cs=FAKE, ld_cs=2, M=64, N=256, K=256)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return _rc(fq, "fp8q_gemm_blockscaled_q", a["A"], a["fa"], a["lda"], a["sA"], a["sA_sm"], a["sA_skb"],
+                   a["B"], a["fb"], a["ldb"], a["sB"], a["gb"], a["sB_sn"], a["sB_skb"], a["fc"],
+                   ctypes.c_float(a["eps"]), a["Cq"], a["ldcq"], a["Cs"], a["ld_cs"], a["M"], a["N"], a["K"], None)
+
+    assert call(Cs=None)[0] == fq.EINVAL
+    assert call(fc=3)[0] == fq.EINVAL
+    assert call(eps=0.0)[0] == fq.EINVAL
+    rc, msg = call(N=192, ldcq=192)
+    assert rc == fq.ESHAPE and "multiples of 128" in msg
+    assert call(ld_cs=1)[0] == fq.EINVAL
+    assert call(ldcq=128)[0] == fq.EINVAL
+    assert call(Cs=FAKE + 2)[0] == fq.EALIGN

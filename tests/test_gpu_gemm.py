@@ -20,6 +20,7 @@ pytestmark = pytest.mark.gpu
 E4, E5 = 0, 1
 G1, G128 = 1, 2
 TOL = 1e-5
+MAXF = {E4: 448.0, E5: 57344.0}
 
 
 def rand_scales(shape, seed):
@@ -277,15 +278,22 @@ def test_gemm_q_exact_inputs_match_oracle(fq, orc, gpu, fa, fb, gb, fc, M, N, K)
     assert np.array_equal(q, wq)
 
 
-@pytest.mark.parametrize("fa,fb,gb,fc", [(E4, E4, G128, E4), (E5, E4, G1, E5)])
-def test_gemm_q_equals_gemm_then_quantize(fq, orc, gpu, fa, fb, gb, fc):
+@pytest.mark.parametrize("fa,fb,gb,fc,special", [(E4, E4, G128, E4, False), (E5, E4, G1, E5, False),
+                                                 (E4, E4, G128, E4, True)])
+def test_gemm_q_equals_gemm_then_quantize(fq, orc, gpu, fa, fb, gb, fc, special):
     """Random codes over the whole code space and random scales: the fused
     output is bit for bit fp8q_quantize_1x128 of fp8q_gemm_blockscaled's
     fp32 C (the same accumulation, quantized in registers instead of after
-    a round trip through HBM)."""
+    a round trip through HBM).  The special case puts a NaN code in one A
+    row and one B row (NaN blocks: codes 0x7F, NaN scales) and a zero A row
+    (zero blocks: codes 0x00, scale eps/MAX)."""
     M, N, K = 300, 640, 768
     A = W.fp8_codes((M, K), fa, seed=71)
     B = W.fp8_codes((N, K), fb, seed=72)
+    if special:
+        A[3, 5] = 0x7F
+        B[200, 77] = 0xFF
+        A[10, :] = 0
     sA = rand_scales((M, K // 128), 73)
     sB = rand_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 74)
     q, s = run_gemm_q(fq, A, fa, sA, B, fb, sB, gb, fc)
@@ -296,6 +304,13 @@ def test_gemm_q_equals_gemm_then_quantize(fq, orc, gpu, fa, fb, gb, fc):
     torch.cuda.synchronize()
     assert np.array_equal(s.view(np.uint32), s2.cpu().numpy().view(np.uint32))
     assert np.array_equal(q, q2.cpu().numpy())
+    if special:
+        assert np.all(q[3] == 0x7F) and np.all(np.isnan(s[3])) and np.all(q[:, 200] == 0x7F)
+        # row 10 is zero except in column 200's block (0 * NaN is NaN)
+        z = np.float32(np.float32(1e-12) / np.float32(MAXF[fc]))
+        assert np.all(q[10, :128] == 0) and np.all(q[10, 256:] == 0) and np.all(q[10, 128:256] == 0x7F)
+        assert s[10, 0] == z and np.all(s[10, 2:] == z) and np.isnan(s[10, 1])
+        return
     # and against the oracle, through the error bound of the GEMM
     Cref, D = orc.gemm_blockscaled(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb)
     check(C.cpu(), Cref, D, "unfused C")
