@@ -68,3 +68,65 @@ def test_graph_replay_matches_eager(fq, gpu):
         x.mul_(1.75)
         X.mul_(-0.5)
         torch.cuda.synchronize()
+
+
+def test_graph_replay_mx_and_fused_epilogue(fq, gpu):
+    """MX quantize + MX GEMM, the GEMM with the 1x128 epilogue and an EMA
+    scaler step, captured once and replayed against eager calls, with the
+    inputs changed in place between replays."""
+    dev = gpu
+    M, N, K = 256, 384, 1024
+    X = W.activation(M, K, seed=911, factor=1e3, dtype=torch.bfloat16, device=dev)
+    w = W.weight(N, K, seed=912, device=dev)
+    qW = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    sW = torch.empty(N // 128, K // 128, dtype=torch.float32, device=dev)
+    fq.fp8q_quantize_128x128(w, N, K, K, E4, 1e-12, qW, K, sW, K // 128)
+    qWm = torch.empty(N, K, dtype=torch.uint8, device=dev)
+    sWm = torch.empty(N, K // 32, dtype=torch.uint8, device=dev)
+    fq.fp8q_quantize_mx(w, N, K, K, E4, qWm, K, sWm, K // 32)
+    x = W.delayed_step(512, 1024, 2.0, seed=913, device=dev)
+
+    def buffers():
+        b = {
+            "qm": torch.empty(M, K, dtype=torch.uint8, device=dev),
+            "sm": torch.empty(M, K // 32, dtype=torch.uint8, device=dev),
+            "Cm": torch.empty(M, N, dtype=torch.bfloat16, device=dev),
+            "qX": torch.empty(M, K, dtype=torch.uint8, device=dev),
+            "sX": torch.empty(M, K // 128, dtype=torch.float32, device=dev),
+            "qC": torch.empty(M, N, dtype=torch.uint8, device=dev),
+            "sC": torch.empty(M, N // 128, dtype=torch.float32, device=dev),
+            "st": torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev),
+            "am": torch.zeros(1, dtype=torch.float32, device=dev),
+            "q": torch.empty(x.numel(), dtype=torch.uint8, device=dev),
+        }
+        fq.fp8q_delayed_scaler_init_stat(b["st"], 4, 448.0, 1e-12, 1.0, fq.STAT_EMA, 0.25)
+        return b
+
+    def step(b):
+        fq.fp8q_quantize_mx(X, M, K, K, E4, b["qm"], K, b["sm"], K // 32)
+        fq.fp8q_gemm_mx(b["qm"], E4, K, b["sm"], K // 32, qWm, E4, K, sWm, K // 32, b["Cm"], N, M, N, K)
+        fq.fp8q_quantize_1x128(X, M, K, K, E4, 1e-12, b["qX"], K, b["sX"], K // 128)
+        fq.fp8q_gemm_blockscaled_q(b["qX"], E4, K, b["sX"], K // 128, 1, qW, E4, K, sW, 2, K // 128, 1, E4, 1e-12,
+                                   b["qC"], N, b["sC"], N // 128, M, N, K)
+        sc = b["st"].data_ptr() + fq.SCALER_SCALE_OFFSET
+        fq.fp8q_quantize_tensor(x, x.numel(), E4, sc, b["q"], b["am"])
+        fq.fp8q_delayed_scaler_update(b["st"], b["am"])
+
+    bg, be = buffers(), buffers()
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        step(bg)
+    for rep in range(4):
+        gr.replay()
+        torch.cuda.synchronize()
+        step(be)
+        torch.cuda.synchronize()
+        for k in bg:
+            a = bg[k].view(torch.uint8) if bg[k].dtype != torch.uint8 else bg[k]
+            e = be[k].view(torch.uint8) if be[k].dtype != torch.uint8 else be[k]
+            assert torch.equal(a, e), f"replay {rep}: {k} differs from the eager result"
+        X.mul_(-1.5)
+        x.mul_(0.5)
+        torch.cuda.synchronize()
