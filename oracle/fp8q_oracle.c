@@ -236,6 +236,7 @@ void orc_dequantize(const uint8_t* q, int fmt, int64_t rows, int64_t cols, int64
       else if (gran == ORC_GRAN_1x128) s = scales[r * ld_s + c / 128];
       else s = scales[(r / 128) * ld_s + c / 128];
       float v = (float)(orc_decode(q[r * ldq + c], fmt) * (double)s);
+      if (isnan(v)) v = canonical_nan();  /* a NaN the library writes is the quiet NaN */
       if (out_dt == ORC_F32) ((float*)y)[r * ldy + c] = v;
       else ((uint16_t*)y)[r * ldy + c] = f32_to_bf16_rne(v);
     }

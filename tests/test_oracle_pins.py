@@ -323,6 +323,25 @@ def test_dequantize_is_one_float32_product(orc, fmt):
     assert np.array_equal(yb, refb)
 
 
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_dequantize_nan_results_are_the_quiet_nan(orc, fmt):
+    """Every NaN the dequantizer writes is the quiet NaN 0x7FC00000 (0x7FC0
+    in bf16), whatever produced it: a NaN code, 0 * Inf (scale +Inf) or a
+    NaN scale; +Inf scales give signed infinities for nonzero codes."""
+    nan_code = 0x7F
+    q = np.array([[0x00, 0x80, nan_code, 0x38, 0xB8]], np.uint8)  # +0, -0, NaN, +1 (E4) / +0.5.. (E5), -
+    for s, want_inf in ((np.float32(np.inf), True), (np.float32(np.nan), False), (np.float32(-np.inf), True)):
+        y = orc.dequantize(q, fmt, np.array([s], np.float32), orc.GRAN_TENSOR).reshape(-1)
+        bits = y.view(np.uint32)
+        if want_inf:
+            assert bits[0] == bits[1] == bits[2] == 0x7FC00000
+            assert np.isinf(y[3]) and np.isinf(y[4]) and np.sign(y[3]) == -np.sign(y[4])
+        else:
+            assert np.all(bits == 0x7FC00000)
+        yb = orc.dequantize(q, fmt, np.array([s], np.float32), orc.GRAN_TENSOR, out_bf16=True).reshape(-1)
+        assert np.all(yb[:3] == 0x7FC0)
+
+
 # ------------------------------------------------------------------ delayed scaler
 def test_delayed_scaler_ramp_closed_form(orc):
     """PyTorch-native FP8 article, section 4.2 DelayedScaler(window=16): the
