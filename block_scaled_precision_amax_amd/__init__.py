@@ -43,6 +43,7 @@ SYMBOLS = (
     "fp8q_gemm_blockscaled_fast",
     "fp8q_gemm_mx",
     "fp8q_gemm_blockscaled_q",
+    "fp8q_quantize_tensor_dq",
 )
 
 
@@ -99,6 +100,7 @@ def lib() -> ctypes.CDLL:
             "fp8q_gemm_blockscaled_fast": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64,
                                                  vp, i32, i64, i64, i64, i64, vp]),
             "fp8q_gemm_mx": (i32, [vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp, i32, i64, i64, i64, i64, vp]),
+            "fp8q_quantize_tensor_dq": (i32, [vp, i32, i64, i32, vp, vp, vp, vp, i32, vp]),
             "fp8q_gemm_blockscaled_q": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64, i32, f32,
                                               vp, i64, vp, i64, i64, i64, i64, vp]),
         }
@@ -223,3 +225,8 @@ def fp8q_gemm_blockscaled_q(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb, s
     _check(lib().fp8q_gemm_blockscaled_q(_ptr(A), fa, lda, _ptr(sA), sA_sm, sA_skb, _ptr(B), fb, ldb, _ptr(sB), gb,
                                          sB_sn, sB_skb, fc, eps, _ptr(Cq), ldcq, _ptr(Cs), ld_cs, M, N, K,
                                          _stream(stream, A)))
+
+
+def fp8q_quantize_tensor_dq(x, n, f, scale, q, y, amax_acc=None, stream=None) -> None:
+    _check(lib().fp8q_quantize_tensor_dq(_ptr(x), _dt(x), n, f, _ptr(scale), _ptr(q), _ptr(amax_acc), _ptr(y),
+                                         _dt(y), _stream(stream, x)))

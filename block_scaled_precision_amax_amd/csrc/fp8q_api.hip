@@ -111,6 +111,18 @@ int fp8q_quantize_tensor(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f,
   return launch_quantize_tensor(x, dt, n, f, scale, q, amax_acc, S(stream));
 }
 
+int fp8q_quantize_tensor_dq(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
+                            uint8_t* q, float* amax_acc, void* y, fp8q_dtype out_dt, void* stream) {
+  if (!x || !scale || !q || !y) return fail(FP8Q_EINVAL, "quantize_tensor_dq: null pointer");
+  if (!valid_dt(dt) || !valid_fmt(f) || !valid_dt(out_dt))
+    return fail(FP8Q_EINVAL, "quantize_tensor_dq: bad dtype or format");
+  if (n <= 0) return fail(FP8Q_EINVAL, "quantize_tensor_dq: n must be positive");
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(scale, 4) ||
+      (amax_acc && !aligned(amax_acc, 4)))
+    return fail(FP8Q_EALIGN, "quantize_tensor_dq: x, q and y must be 16-byte aligned");
+  return launch_quantize_tensor(x, dt, n, f, scale, q, amax_acc, S(stream), y, out_dt);
+}
+
 int fp8q_quantize_1x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
                         fp8q_format f, float eps, uint8_t* q, int64_t ldq, float* scales,
                         int64_t ld_s, void* stream) {

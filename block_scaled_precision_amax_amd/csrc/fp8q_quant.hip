@@ -153,13 +153,48 @@ __device__ __forceinline__ uint32_t quant4_exact(float a, float b, float c, floa
          (enc1<FMT>(d / s) << 24);
 }
 
+// Code -> fp32 (exact, two codes per conversion) and the canonical NaN.
+template <int FMT>
+__device__ __forceinline__ float2 dec2(uint32_t w, bool hi) {
+  if constexpr (FMT == FP8Q_E4M3FN) {
+    auto t = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    return make_float2(t[0], t[1]);
+  } else {
+    auto t = hi ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+    return make_float2(t[0], t[1]);
+  }
+}
+
+__device__ __forceinline__ float canon_nan(float f) {
+  return f != f ? __uint_as_float(0x7FC00000u) : f;
+}
+
+// Dequantized values of one codes word (4 codes), y = fl32(dec(q) * s) with
+// NaN made 0x7FC00000, written as fp32 or RNE bf16 at element i4 of y --
+// the arithmetic of fp8q_dequantize, so the fused output matches it bit
+// for bit.
+template <int FMT, int ODT>
+__device__ __forceinline__ void store_dq4(uint32_t w, float s, void* __restrict__ y, int64_t i4) {
+  const float2 lo = dec2<FMT>(w, false), hi = dec2<FMT>(w, true);
+  const float o0 = canon_nan(lo.x * s), o1 = canon_nan(lo.y * s), o2 = canon_nan(hi.x * s), o3 = canon_nan(hi.y * s);
+  if constexpr (ODT == FP8Q_F32) {
+    __builtin_nontemporal_store(u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)},
+                                (u32x4*)((float*)y + i4));
+  } else {
+    const uint32_t a = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o0, (__bf16)o1});
+    const uint32_t b = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o2, (__bf16)o3});
+    __builtin_nontemporal_store(u32x2{a, b}, (u32x2*)((uint16_t*)y + i4));
+  }
+}
+
 // The stream of one per-tensor quantization.  FAST selects, once for the
 // whole tensor, the corrected-reciprocal division (scale in [2^-80, 2^80])
 // or IEEE division for every element; a vector holding a NaN is re-encoded
 // element by element either way.  Returns the lane's max |x| bit pattern.
-template <int DT, int FMT, bool FAST>
+// ODT >= 0 also writes the dequantized codes to y (fp32 or bf16).
+template <int DT, int FMT, bool FAST, int ODT>
 __device__ __forceinline__ uint32_t tensor_stream(const u32x4* __restrict__ xv, int64_t nvec, float s,
-                                                  float r, uint8_t* __restrict__ q) {
+                                                  float r, uint8_t* __restrict__ q, void* __restrict__ y) {
   constexpr int kU = FP8Q_KU_T;
   constexpr int64_t kChunk = (int64_t)kU * kThreads;
   uint32_t m = 0;
@@ -181,6 +216,7 @@ __device__ __forceinline__ uint32_t tensor_stream(const u32x4* __restrict__ xv, 
         uint32_t w = FAST ? quant4_fast<FMT>(a, b, c4, d, s, r) : quant4_exact<FMT>(a, b, c4, d, s);
         if (mv > 0x7F800000u) w = quant4_exact<FMT>(a, b, c4, d, s);
         __builtin_nontemporal_store(w, (uint32_t*)q + i);
+        if constexpr (ODT >= 0) store_dq4<FMT, ODT>(w, s, y, 4 * i);
       } else {
         const uint32_t mv = pk_fold(vec_absmax<DT>(0u, v[u]));
         m = max(m, mv);
@@ -194,30 +230,43 @@ __device__ __forceinline__ uint32_t tensor_stream(const u32x4* __restrict__ xv, 
           w.y = quant4_exact<FMT>(e4, e5, e6, e7, s);
         }
         __builtin_nontemporal_store(w, (u32x2*)q + i);
+        if constexpr (ODT >= 0) {
+          store_dq4<FMT, ODT>(w.x, s, y, 8 * i);
+          store_dq4<FMT, ODT>(w.y, s, y, 8 * i + 4);
+        }
       }
     }
   }
   return m;
 }
 
-template <int DT, int FMT>
+template <int DT, int FMT, int ODT>
 __global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restrict__ x, int64_t n,
                                                            const float* __restrict__ scale,
                                                            uint8_t* __restrict__ q,
-                                                           uint32_t* __restrict__ amax_acc) {
+                                                           uint32_t* __restrict__ amax_acc,
+                                                           void* __restrict__ y) {
   const float s = *scale;
   const float r = 1.0f / s;
   const int64_t per_vec = DT == FP8Q_F32 ? 4 : 8;
   const int64_t nvec = n / per_vec;
   const u32x4* xv = (const u32x4*)x;
-  uint32_t m = scale_ok(s) ? tensor_stream<DT, FMT, true>(xv, nvec, s, r, q)
-                           : tensor_stream<DT, FMT, false>(xv, nvec, s, r, q);
+  uint32_t m = scale_ok(s) ? tensor_stream<DT, FMT, true, ODT>(xv, nvec, s, r, q, y)
+                           : tensor_stream<DT, FMT, false, ODT>(xv, nvec, s, r, q, y);
   if (blockIdx.x == 0) {
     for (int64_t j = nvec * per_vec + threadIdx.x; j < n; j += kThreads) {
       uint32_t b = DT == FP8Q_F32 ? ((const uint32_t*)x)[j]
                                   : (uint32_t)((const uint16_t*)x)[j] << 16;
       m = max(m, b & 0x7FFFFFFFu);
-      q[j] = (uint8_t)enc1<FMT>(__uint_as_float(b) / s);
+      const uint32_t c = enc1<FMT>(__uint_as_float(b) / s);
+      q[j] = (uint8_t)c;
+      if constexpr (ODT >= 0) {
+        const float o = canon_nan(dec2<FMT>(c, false).x * s);
+        if constexpr (ODT == FP8Q_F32)
+          ((float*)y)[j] = o;
+        else
+          ((uint16_t*)y)[j] = __builtin_bit_cast(uint16_t, (__bf16)o);
+      }
     }
   }
   if (amax_acc) {
@@ -604,20 +653,6 @@ __global__ __launch_bounds__(64) void k_scaler_update(fp8q_scaler* st, uint32_t*
 }
 
 // ---------------------------------------------------------------- dequantize
-template <int FMT>
-__device__ __forceinline__ float2 dec2(uint32_t w, bool hi) {
-  if constexpr (FMT == FP8Q_E4M3FN) {
-    auto t = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
-    return make_float2(t[0], t[1]);
-  } else {
-    auto t = hi ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true) : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
-    return make_float2(t[0], t[1]);
-  }
-}
-
-__device__ __forceinline__ float canon_nan(float f) {
-  return f != f ? __uint_as_float(0x7FC00000u) : f;
-}
 
 // Work unit: (row, chunk of kThreads*8*FP8Q_KU_D columns); each thread
 // handles FP8Q_KU_D groups of 8 codes, lane l at codes 8l .. 8l+8 of the
@@ -838,21 +873,32 @@ int launch_amax(const void* x, int dt, int64_t n, float* amax, hipStream_t st) {
 
 template <int DT, int FMT>
 static void launch_qt(int grid, const void* x, int64_t n, const float* scale, uint8_t* q,
-                      float* amax_acc, hipStream_t st) {
-  hipLaunchKernelGGL((k_quant_tensor<DT, FMT>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
-                     (uint32_t*)amax_acc);
+                      float* amax_acc, hipStream_t st, void* y = nullptr, int out_dt = -1) {
+  if (out_dt == FP8Q_F32)
+    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, FP8Q_F32>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+                       (uint32_t*)amax_acc, y);
+  else if (out_dt == FP8Q_BF16)
+    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, FP8Q_BF16>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+                       (uint32_t*)amax_acc, y);
+  else
+    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, -1>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+                       (uint32_t*)amax_acc, y);
 }
 
 int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const float* scale, uint8_t* q,
-                           float* amax_acc, hipStream_t st) {
+                           float* amax_acc, hipStream_t st, void* y, int out_dt) {
   const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
   const int64_t ch = (int64_t)FP8Q_KU_T * kThreads;
   const int grid = chunk_grid((nvec + ch - 1) / ch, FP8Q_G_T);
-  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st);
-  else if (dt == FP8Q_F32) launch_qt<FP8Q_F32, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st);
-  else if (fmt == FP8Q_E4M3FN) launch_qt<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st);
-  else launch_qt<FP8Q_BF16, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st);
-  return check_launch("quantize_tensor");
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN)
+    launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+  else if (dt == FP8Q_F32)
+    launch_qt<FP8Q_F32, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+  else if (fmt == FP8Q_E4M3FN)
+    launch_qt<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+  else
+    launch_qt<FP8Q_BF16, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+  return check_launch(y ? "quantize_tensor_dq" : "quantize_tensor");
 }
 
 template <int DT, int FMT>

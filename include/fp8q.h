@@ -112,6 +112,16 @@ int fp8q_amax(const void* x, fp8q_dtype dt, int64_t n, float* amax, void* stream
 int fp8q_quantize_tensor(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
                          uint8_t* q, float* amax_acc, void* stream);
 
+/* fp8q_quantize_tensor that also writes the round trip: y = fl32(dec(q) * s)
+ * (fp32, or rounded to nearest-even bf16; NaN -> the quiet NaN), bit for bit
+ * what fp8q_dequantize makes of the codes, in the same pass over x -- the
+ * handbook's quant ([H]: (x / s).clamp().to(FP8).float() * s) and the
+ * quantize-dequantize of a fake-quantized forward copy ([A] 4.2).
+ * y: n elements of out_dt, 16-B aligned; other arguments and errors as
+ * fp8q_quantize_tensor. */
+int fp8q_quantize_tensor_dq(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
+                            uint8_t* q, float* amax_acc, void* y, fp8q_dtype out_dt, void* stream);
+
 /* Fine-grained 1x128 quantization of activations ([H] per_block(x, 1,
  * 128); DeepSeek-V3 activation tiling).  For row r and column block kb:
  *   s = scale(amax(x[r, 128kb : 128kb+128]), eps), q = enc(fl32(x/s)).

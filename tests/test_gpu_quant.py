@@ -180,6 +180,45 @@ def test_quantize_tensor(fq, orc, gpu, dtype, fmt):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
+def test_quantize_tensor_round_trip(fq, orc, gpu, dtype, fmt, out):
+    """fp8q_quantize_tensor_dq: codes as fp8q_quantize_tensor, the round
+    trip as the oracle's dequantize of those codes (fp32 bit for bit; bf16
+    as its RNE, NaN as 0x7FC0), a ragged length (tail elements), NaN / Inf /
+    signed zeros, every scale regime, and the fused amax."""
+    n = 100_003
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(n) * np.exp(rng.standard_normal(n) * 4)).astype(np.float32)
+    x[::97] = 0.0
+    x[1::97] = -0.0
+    x[5] = np.nan
+    x[6] = np.inf
+    x[n - 1] = -np.inf
+    x[n - 2] = np.nan
+    xt = torch.from_numpy(x).to(dtype)
+    xd = xt.to(gpu)
+    xn = W.to_numpy_input(xt)
+    q = torch.empty(n, dtype=torch.uint8, device=gpu)
+    y = torch.empty(n, dtype=out, device=gpu)
+    acc = torch.zeros(1, dtype=torch.float32, device=gpu)
+    for s in SCALES:
+        sd = torch.tensor([s], dtype=torch.float32, device=gpu)
+        fq.fp8q_quantize_tensor_dq(xd, n, fmt, sd, q, y, acc)
+        torch.cuda.synchronize()
+        wq = orc.quantize_tensor(xn, fmt, float(np.float32(s))).reshape(-1)
+        assert_codes_equal(q.cpu().numpy(), wq, f"s={s}")
+        sc = np.array([s], np.float32)
+        if out == torch.float32:
+            wy = orc.dequantize(wq.reshape(1, -1), fmt, sc, orc.GRAN_TENSOR).reshape(-1)
+            assert np.array_equal(f32bits(y.cpu().numpy()), f32bits(wy)), f"s={s}"
+        else:
+            wy = orc.dequantize(wq.reshape(1, -1), fmt, sc, orc.GRAN_TENSOR, out_bf16=True).reshape(-1)
+            assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), wy), f"s={s}"
+    assert f32bits(acc.cpu().numpy())[0] == 0x7FC00000  # x holds NaN
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_quantize_tensor_running_amax(fq, orc, gpu, dtype):
     x = W.normal((77_777,), seed=3, std=5.0, dtype=dtype)
     xd = x.to(gpu)
