@@ -88,6 +88,56 @@ __device__ __forceinline__ v8bf dec8_bf16(u32x2 w) {
   return r;
 }
 
+// With an E5M2 operand the exact path multiplies in f16 instead: an E5M2
+// code is the upper byte of the f16 of the same value, so its conversion
+// is one byte permute per two codes (against one 8-cycle conversion on
+// the bf16 side); E4M3FN codes then convert to f16, also exactly (range
+// 2^-9 .. 448, three mantissa bits).  f16 x f16 products are exact in
+// fp32 like bf16 x bf16 ones, so the block sums are the same.
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+template <bool H16>
+struct Mf;
+template <>
+struct Mf<false> {
+  using v8 = v8bf;
+  using v2 = v2bf;
+};
+template <>
+struct Mf<true> {
+  using v8 = v8h;
+  using v2 = v2h;
+};
+
+template <int FMT, bool H16, bool HI>
+__device__ __forceinline__ typename Mf<H16>::v2 dec2x(uint32_t w) {
+  if constexpr (!H16)
+    return dec2_bf16<FMT, HI>(w);
+  else if constexpr (FMT == FP8Q_E4M3FN)
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)w, 1.0f, HI);
+  else  // bytes 0,1 (or 2,3) of w into the upper bytes of two f16 halves
+    return __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0u, w, HI ? 0x030C020Cu : 0x010C000Cu));
+}
+
+template <int FMT, bool H16>
+__device__ __forceinline__ typename Mf<H16>::v8 dec8x(u32x2 w) {
+  using V2 = typename Mf<H16>::v2;
+  const V2 a = dec2x<FMT, H16, false>(w.x), b = dec2x<FMT, H16, true>(w.x);
+  const V2 c = dec2x<FMT, H16, false>(w.y), d = dec2x<FMT, H16, true>(w.y);
+  typename Mf<H16>::v8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+template <bool H16>
+__device__ __forceinline__ v4f mfma16x32(typename Mf<H16>::v8 a, typename Mf<H16>::v8 b, v4f c) {
+  if constexpr (H16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // An empty asm that claims to read and rewrite v: the value must exist in
 // registers at this point of the program, which keeps the compiler from
 // sinking or batching the pure MFMA / FMA arithmetic around it and so keeps
@@ -376,20 +426,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
         r[2] = u32x2{x1.x, x1.y};
         r[3] = u32x2{x1.z, x1.w};
       };
-      v8bf fb[TJ][4];
+      constexpr bool H16 = FA == FP8Q_E5M2 || FB == FP8Q_E5M2;
+      using V8 = typename Mf<H16>::v8;
+      using V2 = typename Mf<H16>::v2;
+      V8 fb[TJ][4];
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         u32x2 r[4];
         raw32(lb + 16 * j * BK, r);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) fb[j][kk] = dec8_bf16<FB>(r[kk]);
+        for (int kk = 0; kk < 4; ++kk) fb[j][kk] = dec8x<FB, H16>(r[kk]);
       }
-      v8bf fa[4];
+      V8 fa[4];
       {
         u32x2 r[4];
         raw32(la, r);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) fa[kk] = dec8_bf16<FA>(r[kk]);
+        for (int kk = 0; kk < 4; ++kk) fa[kk] = dec8x<FA, H16>(r[kk]);
       }
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
@@ -399,13 +452,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
           raw32(la + 16 * (i + 1) * BK, raw);
           cn = coef(i + 1);
         }
-        v2bf part[4][4];
+        V2 part[4][4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
-            pn[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[kk], fb[j][kk],
-                                                            kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j], 0, 0, 0);
+            pn[j] = mfma16x32<H16>(fa[kk], fb[j][kk], kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j]);
             pin(pn[j]);
             if (i > 0) {
               fold(i - 1, j, kk, pp[j][kk], cp);
@@ -414,14 +466,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
             if (i + 1 < TI) {
               // decode part j (two codes) of the next row tile's fragment kk
               const uint32_t w = (j & 2) ? raw[kk].y : raw[kk].x;
-              part[kk][j] = (j & 1) ? dec2_bf16<FA, true>(w) : dec2_bf16<FA, false>(w);
+              part[kk][j] = (j & 1) ? dec2x<FA, H16, true>(w) : dec2x<FA, H16, false>(w);
             }
             __builtin_amdgcn_sched_barrier(0);
           }
         if (i + 1 < TI) {
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            v8bf f;
+            V8 f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               f[2 * q] = part[kk][q][0];
