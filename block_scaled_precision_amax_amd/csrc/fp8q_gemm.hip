@@ -591,7 +591,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
     const uint8_t* __restrict__ B, int64_t ldb, const uint8_t* __restrict__ sB, int64_t ld_sb,
     void* __restrict__ C, int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t ntm, int64_t ntn) {
   constexpr int BM = 256, BN = 256, TI = 8, TJ = 4;
-  constexpr int NLOAD = BM / 64 + BN / 64 + 1;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[2][BM * BK];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_b[2][BN * BK];
   __shared__ __attribute__((aligned(16))) uint8_t lds_sa[2][BM * 4];
@@ -671,7 +670,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
     st ^= 1;
   }
   compute(st);
-  (void)NLOAD;
 
   // ---- epilogue: 16x16 results, column l%16, rows 4*(l/16) + e
 #pragma unroll
