@@ -223,3 +223,21 @@ def test_gemm_q_validation(fq):
     assert call(ld_cs=1)[0] == fq.EINVAL
     assert call(ldcq=128)[0] == fq.EINVAL
     assert call(Cs=FAKE + 2)[0] == fq.EALIGN
+
+
+def test_gemm_operand_span_limit(fq):
+    """Operands of 4 GiB or more are refused before any launch (the LDS copies
+    take 32-bit byte offsets)."""
+    M, K = 1 << 20, 8192  # (M - 1) * lda + K > 2^32
+    rc, msg = _rc(fq, "fp8q_gemm_blockscaled", FAKE, 0, K, FAKE, K // 128, 1, FAKE, 0, K, FAKE, 2, K // 128, 1,
+                  FAKE, 0, 256, M, 256, K, None)
+    assert rc == fq.ESHAPE and "4 GiB" in msg
+    rc, msg = _rc(fq, "fp8q_gemm_blockscaled_fast", FAKE, 0, K, FAKE, K // 128, 1, FAKE, 0, K, FAKE, 2, K // 128,
+                  1, FAKE, 0, M, 256, M, K, None)  # B spans 4 GiB
+    assert rc == fq.ESHAPE and "4 GiB" in msg
+    rc, msg = _rc(fq, "fp8q_gemm_mx", FAKE, 0, K, FAKE, K // 32, FAKE, 0, K, FAKE, K // 32, FAKE, 0, 256, M, 256, K,
+                  None)
+    assert rc == fq.ESHAPE and "4 GiB" in msg
+    rc, msg = _rc(fq, "fp8q_gemm_blockscaled_q", FAKE, 0, K, FAKE, K // 128, 1, FAKE, 0, K, FAKE, 2, K // 128, 1, 0,
+                  ctypes.c_float(1e-12), FAKE, 256, FAKE, 2, M, 256, K, None)
+    assert rc == fq.ESHAPE and "4 GiB" in msg
