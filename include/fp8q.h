@@ -278,12 +278,15 @@ int fp8q_gemm_blockscaled_q(const uint8_t* A, fp8q_format fa, int64_t lda, const
                             int64_t ldcq, float* Cs, int64_t ld_cs, int64_t M, int64_t N, int64_t K,
                             void* stream);
 
-/* MX GEMM: C[m,n] = sum over 32-element K blocks kb of
+/* MX GEMM ([H] FP8 training, hardware note: 32 elements share one scale
+ * factor in hardware): C[m,n] = sum over 32-element K blocks kb of
  *   2^(sA[m,kb] - 127) * 2^(sB[n,kb] - 127) * sum_{k in kb} dec(A[m,k]) dec(B[n,k]),
  * the product of two fp8q_quantize_mx outputs (B as [N,K], K-contiguous).
  * The scaled FP8 MFMA of gfx950 applies both scales and accumulates the
  * whole K in fp32; like fp8q_gemm_blockscaled_fast it is bounded by
- * |C - C_exact| <= 2^-10 * D, D the same sum over |terms|.
+ * |C - C_exact| <= 2^-10 * D, D the same sum over |terms|, while the scaled
+ * terms stay in fp32's normal range (products of two scales far from 1 can
+ * underflow to zero or overflow to Inf in fp32).
  * A [M,K] codes, lda; B [N,K] codes, ldb (16-B aligned rows); sA [M, K/32]
  * and sB [N, K/32] E8M0 bytes with row strides ld_sa, ld_sb (multiples of
  * 4, >= K/32); K % 128 == 0; M, N free.  C [M,N] fp32 or bf16 (RNE), ldc.
