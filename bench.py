@@ -55,6 +55,10 @@ COPY_ELEMS = 1 << 28             # fp32 copy reference: 1 GiB read + 1 GiB writt
 # passes over this same command, scaled by what the counters read for the
 # copy reference; valid only for the kernel source the counters were taken on.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_blockscaled_16384x18432x7168_hbm_traffic.md")
+# MFMA-pipe busy fraction of the same kernel from one rocprofv3 counter pass
+# (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE cycles x 1024 SIMDs), with the
+# same validity rule.
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_blockscaled_16384x18432x7168_mfma_counters.md")
 GEMM_SOURCES = ("block_scaled_precision_amax_amd/csrc/fp8q_gemm.hip",
                 "block_scaled_precision_amax_amd/csrc/fp8q_internal.h")
 
@@ -86,17 +90,22 @@ def gemm_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """Counter-measured HBM bytes per GEMM launch, or None when the summary is
+def counter_field(path, name, kind):
+    """A field of a committed counter summary, or None when the summary is
     missing or was taken on different GEMM source."""
     try:
-        with open(TRAFFIC_SUMMARY) as f:
+        with open(path) as f:
             fields = dict(re.findall(r"^- (\w+): (\S+)\s*$", f.read(), re.M))
     except OSError:
         return None
-    if fields.get("source_sha256") != gemm_source_sha256() or "traffic_bytes_per_launch" not in fields:
+    if fields.get("source_sha256") != gemm_source_sha256() or name not in fields:
         return None
-    return int(fields["traffic_bytes_per_launch"])
+    return kind(fields[name])
+
+
+def measured_traffic():
+    """Counter-measured HBM bytes per GEMM launch (or None)."""
+    return counter_field(TRAFFIC_SUMMARY, "traffic_bytes_per_launch", int)
 
 
 def run_gpu(steps: int, warmup: int):
@@ -441,6 +450,8 @@ def main():
             "achieved": round(gemm_tflops, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gemm_tflops / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
             "traffic_unit": "bytes per launch", "algorithmic_bytes": alg["gemm_bytes"],
+            "mfma_busy": counter_field(MFMA_SUMMARY, "mfma_busy", float),
+            "mfma_busy_clock_ghz": counter_field(MFMA_SUMMARY, "clock_ghz", float),
         },
         "kernels": {
             "gemm_blockscaled": {"ms": round(per["gemm"], 4), "TFLOP/s": round(gemm_tflops, 2),
