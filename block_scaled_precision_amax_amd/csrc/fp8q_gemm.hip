@@ -338,7 +338,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int lr = lane & 15, lq = lane >> 4;
   const int a_row0 = (wm * TI * 16 + lr) * BK, b_row0 = (wn * TJ * 16 + lr) * BK;
   const int64_t wcol0 = n0 + wn * TJ * 16;  // first column of this wavefront
-  const float* sb_blk = sB + (wcol0 >> 7) * sB_sn;
+  // its 128x128 B-scale row; a wavefront wholly past column N (its results
+  // are never stored) reads the last row instead of one past the array
+  const float* sb_blk = sB + ((wcol0 < N ? wcol0 : N - 1) >> 7) * sB_sn;
   // 1x128 B scales: wavefront w stages columns w*BN/8 .. +BN/8 of the tile
   constexpr int SB_LANES = BN / 8;
   const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);

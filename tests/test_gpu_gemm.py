@@ -56,7 +56,8 @@ def bf16_of(c32):
 
 @pytest.mark.parametrize("fa,fb,gb", [(E4, E4, G128), (E5, E4, G128), (E5, E4, G1), (E4, E5, G128),
                                       (E5, E5, G1), (E4, E4, G1)])
-@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (64, 128, 128), (1, 256, 256), (300, 200, 384)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (64, 128, 128), (1, 256, 256), (300, 200, 384), (5, 1, 128),
+                                   (33, 130, 256)])
 def test_gemm_random_codes(fq, orc, gpu, fa, fb, gb, M, N, K):
     """Uniformly random finite codes (the whole code space), random scales,
     ragged M and N, several K blocks."""
@@ -206,7 +207,7 @@ def run_gemm_fast(fq, A, fa, sA, B, fb, sB, gb, out=torch.float32, dev="cuda"):
 
 
 @pytest.mark.parametrize("fa,fb,gb", [(E4, E4, G128), (E5, E4, G128), (E5, E4, G1), (E4, E5, G1)])
-@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (300, 200, 384)])
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (300, 200, 384), (5, 1, 128), (33, 130, 256)])
 def test_gemm_fast_random_codes(fq, orc, gpu, fa, fb, gb, M, N, K):
     A = W.fp8_codes((M, K), fa, seed=M + K)
     B = W.fp8_codes((N, K), fb, seed=N + K + 1)
