@@ -283,6 +283,57 @@ __device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* l
     }
 }
 
+// bf16 C leaves through LDS.  In the 16x16 MFMA result a lane holds four
+// rows of one column, so storing straight from registers writes 32-byte
+// pieces of a row per instruction; on MI355X such partial lines cost the
+// memory system more than their bytes (a bf16 C took longer to write than
+// an fp32 one, which leaves in 64-byte pieces).  Each wavefront writes its
+// TI*16 x TJ*16 tile into its own LDS region and reads it back 16 bytes per
+// lane, eight lanes per row, so every 128-byte row piece of the tile leaves
+// in one instruction.  In LDS the 16-byte chunk c of row r sits in slot
+// c ^ ((r >> 2) & 7): the four lane groups of a write (rows 4 apart) then
+// fall on different banks, and a read of eight whole rows is conflict-free.
+// Columns past N are not stored; without 16-byte aligned rows, or at a
+// ragged right edge, the chunk is stored element by element.
+template <int TI, int TJ>
+__device__ __forceinline__ void store_bf16_staged(const v4f (&acc)[TI][TJ], uint16_t* stg, int lane,
+                                                  uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
+                                                  int64_t col0, int64_t M, int64_t N) {
+  constexpr int W = TJ * 16, R = TI * 16, CH = W / 8, RPI = 64 / CH;
+  static_assert(CH == 8, "the swizzle assumes 64-column tiles");
+  const int lr = lane & 15, lq = lane >> 4;
+  __syncthreads();  // every wavefront is done reading the K-loop stages
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * i + 4 * lq + e, sw = (r >> 2) & 7;
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = 16 * j + lr;
+        stg[r * W + 8 * ((col >> 3) ^ sw) + (col & 7)] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+      }
+    }
+  __syncthreads();
+  const bool vec = (((uintptr_t)C | (uintptr_t)(ldc * 2)) & 15) == 0;
+  const int rr = lane / CH, c = lane % CH;
+#pragma unroll 4
+  for (int it = 0; it < R / RPI; ++it) {
+    const int r = it * RPI + rr;
+    const u32x4 v = *(const u32x4*)(stg + r * W + 8 * (c ^ ((r >> 2) & 7)));
+    const int64_t row = row0 + r, col = col0 + 8 * c;
+    if (row >= M || col >= N) continue;
+    uint16_t* dst = C + row * ldc + col;
+    if (vec && col + 8 <= N) {
+      __builtin_nontemporal_store(v, (u32x4*)dst);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (col + q < N) dst[q] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+    }
+  }
+}
+
 // One workgroup of eight wavefronts computes a BM x BN tile of C; wavefront
 // (wm, wn) = (w/4, w%4) owns TI x TJ MFMA tiles of 16x16 at rows
 // 16*TI*wm.. and columns 16*TJ*wn.. (64 columns: inside one 128-column
@@ -556,6 +607,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
                                     (uint8_t*)C, ldc, Cs, ld_cs, (wn & 1) == 0);
     return;
   }
+  if constexpr (ODT == FP8Q_BF16) {
+    // staging regions: 2*TI*TJ*256 bytes per wavefront inside the K-loop stages
+    constexpr int WB = TI * 16 * TJ * 16 * 2;
+    static_assert(FAST ? 4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b)
+                       : 8 * WB <= (int)sizeof(lds_b), "bf16 staging does not fit");
+    uint8_t* stg = FAST ? (wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB)
+                        : &lds_b[0][0] + wave * WB;
+    store_bf16_staged<TI, TJ>(acc, (uint16_t*)stg, lane, (uint16_t*)C, ldc, m0 + wm * TI * 16, wcol0, M, N);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int64_t col = wcol0 + 16 * j + lr;
@@ -566,10 +627,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
       for (int e = 0; e < 4; ++e) {
         const int64_t row = m0 + wm * TI * 16 + 16 * i + 4 * lq + e;
         if (row >= M) continue;
-        if constexpr (ODT == FP8Q_F32)
-          __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
-        else
-          __builtin_nontemporal_store((uint16_t)f32_to_bf16(acc[i][j][e]), (uint16_t*)C + row * ldc + col);
+        __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
       }
   }
 }
@@ -674,6 +732,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
   compute(st);
 
   // ---- epilogue: 16x16 results, column l%16, rows 4*(l/16) + e
+  if constexpr (ODT == FP8Q_BF16) {
+    constexpr int WB = TI * 16 * TJ * 16 * 2;
+    static_assert(4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b), "bf16 staging does not fit");
+    uint8_t* stg = wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB;
+    store_bf16_staged<TI, TJ>(acc, (uint16_t*)stg, lane, (uint16_t*)C, ldc, m0 + wm * TI * 16,
+                              n0 + wn * TJ * 16, M, N);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) {
     const int64_t col = n0 + wn * TJ * 16 + 16 * j + lr;
@@ -684,10 +750,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
       for (int e = 0; e < 4; ++e) {
         const int64_t row = m0 + wm * TI * 16 + 16 * i + 4 * lq + e;
         if (row >= M) continue;
-        if constexpr (ODT == FP8Q_F32)
-          __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
-        else
-          __builtin_nontemporal_store((uint16_t)f32_to_bf16(acc[i][j][e]), (uint16_t*)C + row * ldc + col);
+        __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
       }
   }
 }

@@ -86,6 +86,21 @@ def test_gemm_strided_operands(fq, orc, gpu):
     sA = sA_full.t().contiguous()
     Cref, D = orc.gemm_blockscaled(A[:, :K].numpy(), E4, sA.numpy(), B[:, :K].numpy(), E4, sB.numpy(), G128)
     check(C.cpu()[:, :N], Cref, D)
+    # bf16 output into rows with padding (16-byte aligned rows, then rows that
+    # are not): the padding keeps its bytes, the tile equals RNE of the fp32 C
+    for ldc in (N + 8, N + 3):
+        for fast in (False, True):
+            Cb = torch.full((M, ldc), -7.0, dtype=torch.bfloat16, device=gpu)
+            gemm = fq.fp8q_gemm_blockscaled_fast if fast else fq.fp8q_gemm_blockscaled
+            gemm(A.to(gpu), E4, ld, sA_full.to(gpu), 1, M, B.to(gpu), E4, ld, sB.to(gpu), G128, K // 128, 1, Cb, ldc,
+                 M, N, K)
+            C32 = torch.empty(M, N, dtype=torch.float32, device=gpu)
+            gemm(A.to(gpu), E4, ld, sA_full.to(gpu), 1, M, B.to(gpu), E4, ld, sB.to(gpu), G128, K // 128, 1, C32, N,
+                 M, N, K)
+            torch.cuda.synchronize()
+            Cb = Cb.cpu()
+            assert torch.equal(Cb[:, :N].view(torch.int16), C32.cpu().to(torch.bfloat16).view(torch.int16)), (ldc, fast)
+            assert torch.all(Cb[:, N:] == -7.0), (ldc, fast)
 
 
 def test_gemm_special_codes_non_finite(fq, orc, gpu):

@@ -212,6 +212,11 @@ def test_gemm_mx_strided(fq, orc, gpu):
     C = run_gemm_mx(fq, A, E4, sA, B, E4, sB, pad=(32, 128, 4, 12, 5))
     Cref, D = orc.gemm_mx(A.numpy(), E4, sA.numpy(), B.numpy(), E4, sB.numpy())
     check_mx(C, Cref, D, "strided")
+    # bf16 rows padded to 16-byte alignment and not: RNE of the fp32 result,
+    # nothing written past column N
+    for pc in (4, 5):
+        Cb = run_gemm_mx(fq, A, E4, sA, B, E4, sB, out=torch.bfloat16, pad=(32, 128, 4, 12, pc))
+        assert torch.equal(Cb.view(torch.int16), C.to(torch.bfloat16).view(torch.int16)), pc
 
 
 def test_gemm_mx_block_scales_distinct(fq, orc, gpu):
