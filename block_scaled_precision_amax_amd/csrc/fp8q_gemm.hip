@@ -231,10 +231,12 @@ __device__ __forceinline__ void dma_tile(uint8_t* lds, const uint8_t* base, cons
 // division otherwise), saturated, rounded to nearest even, NaN -> 0x7F.
 // Columns past N count as 0 and are not stored.
 template <int QF, int TI, int TJ>
-__device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* lds_rmax, int wave, int lr, int lq,
-                                           int64_t row0, int64_t col0, int64_t M, int64_t N, float eps,
+__device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* lds_rmax, uint8_t* stg, int wave,
+                                           int lane, int64_t row0, int64_t col0, int64_t M, int64_t N, float eps,
                                            uint8_t* __restrict__ Cq, int64_t ldc, float* __restrict__ Cs,
                                            int64_t ld_cs, bool writes_scale) {
+  static_assert(TJ == 4, "64 columns per wavefront");
+  const int lr = lane & 15, lq = lane >> 4;
   uint32_t rm[TI][4];
 #pragma unroll
   for (int i = 0; i < TI; ++i)
@@ -268,69 +270,115 @@ __device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* l
       const int64_t row = row0 + rw;
       const float amax = __uint_as_float(canon_abs_bits(max(rm[i][e], other[rw])));
       const float s = block_scale<QF>(amax, eps);
-      if (row >= M) continue;
-      if (writes_scale && lr == 0 && col0 < N) Cs[row * ld_cs + (col0 >> 7)] = s;
+      if (writes_scale && lr == 0 && col0 < N && row < M) Cs[row * ld_cs + (col0 >> 7)] = s;
       const bool fast = scale_ok(s);
       const float r = 1.0f / s;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        const int64_t col = col0 + 16 * j + lr;
-        if (col >= N) continue;
         const float x = acc[i][j][e];
         const uint32_t c = fast ? (cvt2<QF, false>(sat<QF>(div_rn(x, s, r)), 0.0f, 0u) & 0xFFu) : enc1<QF>(x / s);
-        Cq[row * ldc + col] = (uint8_t)c;
+        // the code goes to LDS (row rw, column 16j+lr; 16-byte chunk j sits
+        // in slot j ^ ((rw >> 2) & 3))
+        stg[rw * 64 + 16 * (j ^ ((rw >> 2) & 3)) + lr] = (uint8_t)c;
       }
     }
+  // The wavefront's codes leave 16 bytes per lane, four lanes per row, so
+  // each row's 64 codes are written by one instruction (stored one by one
+  // from the MFMA layout they left in 16-byte pieces).
+  __syncthreads();
+  const bool vec = (((uintptr_t)Cq | (uintptr_t)ldc) & 15) == 0;
+  const int rr = lane >> 2, c = lane & 3;
+#pragma unroll
+  for (int it = 0; it < TI; ++it) {
+    const int rw = 16 * it + rr;
+    const u32x4 v = *(const u32x4*)(stg + rw * 64 + 16 * (c ^ ((rw >> 2) & 3)));
+    const int64_t row = row0 + rw, col = col0 + 16 * c;
+    if (row >= M || col >= N) continue;
+    uint8_t* dst = Cq + row * ldc + col;
+    if (vec && col + 16 <= N) {
+      __builtin_nontemporal_store(v, (u32x4*)dst);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (col + q < N) dst[q] = (uint8_t)(v[q >> 2] >> (8 * (q & 3)));
+    }
+  }
 }
 
-// bf16 C leaves through LDS.  In the 16x16 MFMA result a lane holds four
-// rows of one column, so storing straight from registers writes 32-byte
-// pieces of a row per instruction; on MI355X such partial lines cost the
-// memory system more than their bytes (a bf16 C took longer to write than
-// an fp32 one, which leaves in 64-byte pieces).  Each wavefront writes its
-// TI*16 x TJ*16 tile into its own LDS region and reads it back 16 bytes per
-// lane, eight lanes per row, so every 128-byte row piece of the tile leaves
-// in one instruction.  In LDS the 16-byte chunk c of row r sits in slot
-// c ^ ((r >> 2) & 7): the four lane groups of a write (rows 4 apart) then
-// fall on different banks, and a read of eight whole rows is conflict-free.
-// Columns past N are not stored; without 16-byte aligned rows, or at a
-// ragged right edge, the chunk is stored element by element.
-template <int TI, int TJ>
-__device__ __forceinline__ void store_bf16_staged(const v4f (&acc)[TI][TJ], uint16_t* stg, int lane,
-                                                  uint16_t* __restrict__ C, int64_t ldc, int64_t row0,
-                                                  int64_t col0, int64_t M, int64_t N) {
-  constexpr int W = TJ * 16, R = TI * 16, CH = W / 8, RPI = 64 / CH;
-  static_assert(CH == 8, "the swizzle assumes 64-column tiles");
+// C leaves through LDS.  In the 16x16 MFMA result a lane holds four rows
+// of one column, so storing straight from registers writes 32-byte (bf16)
+// or 64-byte (fp32) pieces of a row per instruction; on MI355X such partial
+// lines cost the memory system more than their bytes (a bf16 C stored that
+// way took longer to write than an fp32 one).  Each wavefront writes NI row
+// tiles (from row tile I0) of its TI x TJ tile into its own LDS region and
+// reads them back 16 bytes per lane, so every 64-column row piece of the
+// tile (128 bytes of bf16, 256 of fp32) leaves in one instruction.  In LDS
+// the 16-byte chunk c of row r sits in slot c ^ sw(r), chosen so that the
+// four lane groups of a write (rows 4 apart) fall on different banks and a
+// read of whole rows is conflict-free.  Columns past N are not stored;
+// without 16-byte aligned rows, or at a ragged right edge, the chunk is
+// stored element by element.
+template <typename T, int I0, int NI, int TI, int TJ>
+__device__ __forceinline__ void store_staged(const v4f (&acc)[TI][TJ], T* stg, int lane, T* __restrict__ C,
+                                             int64_t ldc, int64_t row0, int64_t col0, int64_t M, int64_t N) {
+  constexpr int ES = (int)sizeof(T), EPC = 16 / ES;  // element size, elements per 16-byte chunk
+  constexpr int W = TJ * 16, R = NI * 16, CH = W / EPC, RPI = 64 / CH;
+  static_assert(W == 64 && (ES == 2 || ES == 4), "64-column tiles of bf16 or fp32");
+  auto sw = [](int r) { return ES == 2 ? (r >> 2) & 7 : ((r >> 2) & 3) << 2; };
   const int lr = lane & 15, lq = lane >> 4;
-  __syncthreads();  // every wavefront is done reading the K-loop stages
+  __syncthreads();  // every wavefront is done with what the region held before
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = 16 * i + 4 * lq + e, sw = (r >> 2) & 7;
+      const int r = 16 * i + 4 * lq + e;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
         const int col = 16 * j + lr;
-        stg[r * W + 8 * ((col >> 3) ^ sw) + (col & 7)] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+        const float v = acc[I0 + i][j][e];
+        T t;
+        if constexpr (ES == 2)
+          t = (T)f32_to_bf16(v);
+        else
+          t = v;
+        stg[r * W + EPC * ((col / EPC) ^ sw(r)) + col % EPC] = t;
       }
     }
   __syncthreads();
-  const bool vec = (((uintptr_t)C | (uintptr_t)(ldc * 2)) & 15) == 0;
+  const bool vec = (((uintptr_t)C | (uintptr_t)(ldc * ES)) & 15) == 0;
   const int rr = lane / CH, c = lane % CH;
 #pragma unroll 4
   for (int it = 0; it < R / RPI; ++it) {
     const int r = it * RPI + rr;
-    const u32x4 v = *(const u32x4*)(stg + r * W + 8 * (c ^ ((r >> 2) & 7)));
-    const int64_t row = row0 + r, col = col0 + 8 * c;
+    const u32x4 v = *(const u32x4*)(stg + r * W + EPC * (c ^ sw(r)));
+    const int64_t row = row0 + 16 * I0 + r, col = col0 + EPC * c;
     if (row >= M || col >= N) continue;
-    uint16_t* dst = C + row * ldc + col;
-    if (vec && col + 8 <= N) {
+    T* dst = C + row * ldc + col;
+    if (vec && col + EPC <= N) {
       __builtin_nontemporal_store(v, (u32x4*)dst);
     } else {
 #pragma unroll
-      for (int q = 0; q < 8; ++q)
-        if (col + q < N) dst[q] = (uint16_t)(v[q >> 1] >> (16 * (q & 1)));
+      for (int q = 0; q < EPC; ++q) {
+        if (col + q >= N) continue;
+        if constexpr (ES == 2)
+          dst[q] = (T)(v[q >> 1] >> (16 * (q & 1)));
+        else
+          dst[q] = __uint_as_float(v[q]);
+      }
     }
+  }
+}
+
+// Both output types: bf16 in one pass, fp32 in two passes of half the row
+// tiles (the same LDS bytes per pass).
+template <int ODT, int TI, int TJ>
+__device__ __forceinline__ void store_c(const v4f (&acc)[TI][TJ], uint8_t* stg, int lane, void* C, int64_t ldc,
+                                        int64_t row0, int64_t col0, int64_t M, int64_t N) {
+  if constexpr (ODT == FP8Q_BF16) {
+    store_staged<uint16_t, 0, TI, TI, TJ>(acc, (uint16_t*)stg, lane, (uint16_t*)C, ldc, row0, col0, M, N);
+  } else {
+    store_staged<float, 0, TI / 2, TI, TJ>(acc, (float*)stg, lane, (float*)C, ldc, row0, col0, M, N);
+    store_staged<float, TI / 2, TI / 2, TI, TJ>(acc, (float*)stg, lane, (float*)C, ldc, row0, col0, M, N);
   }
 }
 
@@ -601,34 +649,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   }
   compute(kb, st);
 
-  // ---- epilogue
+  // ---- epilogue.  Staging regions for C: TI*TJ*512 bytes per wavefront
+  // inside the K-loop stages.
+  constexpr int WB = TI * 16 * TJ * 16 * 2;
+  static_assert(FAST ? 4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b)
+                     : 8 * WB <= (int)sizeof(lds_b), "C staging does not fit");
+  uint8_t* stg = FAST ? (wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB)
+                      : &lds_b[0][0] + wave * WB;
   if constexpr (ODT >= kOutQ) {
-    epilogue_q<ODT - kOutQ, TI, TJ>(acc, lds_rmax, wave, lr, lq, m0 + wm * TI * 16, wcol0, M, N, qeps,
+    epilogue_q<ODT - kOutQ, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps,
                                     (uint8_t*)C, ldc, Cs, ld_cs, (wn & 1) == 0);
-    return;
-  }
-  if constexpr (ODT == FP8Q_BF16) {
-    // staging regions: 2*TI*TJ*256 bytes per wavefront inside the K-loop stages
-    constexpr int WB = TI * 16 * TJ * 16 * 2;
-    static_assert(FAST ? 4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b)
-                       : 8 * WB <= (int)sizeof(lds_b), "bf16 staging does not fit");
-    uint8_t* stg = FAST ? (wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB)
-                        : &lds_b[0][0] + wave * WB;
-    store_bf16_staged<TI, TJ>(acc, (uint16_t*)stg, lane, (uint16_t*)C, ldc, m0 + wm * TI * 16, wcol0, M, N);
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int64_t col = wcol0 + 16 * j + lr;
-    if (col >= N) continue;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm * TI * 16 + 16 * i + 4 * lq + e;
-        if (row >= M) continue;
-        __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
-      }
+  } else {
+    store_c<ODT, TI, TJ>(acc, stg, lane, C, ldc, m0 + wm * TI * 16, wcol0, M, N);
   }
 }
 
@@ -731,28 +763,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
   }
   compute(st);
 
-  // ---- epilogue: 16x16 results, column l%16, rows 4*(l/16) + e
-  if constexpr (ODT == FP8Q_BF16) {
-    constexpr int WB = TI * 16 * TJ * 16 * 2;
-    static_assert(4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b), "bf16 staging does not fit");
-    uint8_t* stg = wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB;
-    store_bf16_staged<TI, TJ>(acc, (uint16_t*)stg, lane, (uint16_t*)C, ldc, m0 + wm * TI * 16,
-                              n0 + wn * TJ * 16, M, N);
-    return;
-  }
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) {
-    const int64_t col = n0 + wn * TJ * 16 + 16 * j + lr;
-    if (col >= N) continue;
-#pragma unroll
-    for (int i = 0; i < TI; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t row = m0 + wm * TI * 16 + 16 * i + 4 * lq + e;
-        if (row >= M) continue;
-        __builtin_nontemporal_store(acc[i][j][e], (float*)C + row * ldc + col);
-      }
-  }
+  // ---- epilogue
+  constexpr int WB = TI * 16 * TJ * 16 * 2;
+  static_assert(4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b), "C staging does not fit");
+  uint8_t* stg = wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB;
+  store_c<ODT, TI, TJ>(acc, stg, lane, C, ldc, m0 + wm * TI * 16, n0 + wn * TJ * 16, M, N);
 }
 
 template <int FA, int FB, int ODT>
