@@ -237,51 +237,51 @@ __device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* l
                                            int64_t ld_cs, bool writes_scale) {
   static_assert(TJ == 4, "64 columns per wavefront");
   const int lr = lane & 15, lq = lane >> 4;
-  uint32_t rm[TI][4];
+  // lane (lr, lq) holds row 16i + lr, columns 16j + 4lq + e: its part of the
+  // row maximum, then the four lane groups' parts (lanes lr + 16k)
+  uint32_t rm[TI];
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < TI; ++i) {
+    uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t m = 0;
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        if (col0 + 16 * j + lr < N) m = max(m, __float_as_uint(acc[i][j][e]) & 0x7FFFFFFFu);
-      rm[i][e] = row16_max(m);
-    }
-  // row 16i + 4lq + e of this wavefront's part; lane lr publishes the
-  // values with 4i + e = lr (mod 16)
+      for (int e = 0; e < 4; ++e)
+        if (col0 + 16 * j + 4 * lq + e < N) m = max(m, __float_as_uint(acc[i][j][e]) & 0x7FFFFFFFu);
+    m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+    rm[i] = max(m, (uint32_t)__shfl_xor((int)m, 32));
+  }
   uint32_t* mine = lds_rmax + wave * TI * 16;
+  if (lq == 0) {
 #pragma unroll
-  for (int k0 = 0; k0 < TI * 4; k0 += 16) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int k = k0; k < k0 + 16 && k < TI * 4; ++k)
-      if (lr == k - k0) v = rm[k >> 2][k & 3];
-    const int k = k0 + lr;
-    if (k < TI * 4) mine[16 * (k >> 2) + 4 * lq + (k & 3)] = v;
+    for (int i = 0; i < TI; ++i) mine[16 * i + lr] = rm[i];
   }
   __syncthreads();
   const uint32_t* other = lds_rmax + (wave ^ 1) * TI * 16;
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+  for (int i = 0; i < TI; ++i) {
+    const int rw = 16 * i + lr;
+    const int64_t row = row0 + rw;
+    const float amax = __uint_as_float(canon_abs_bits(max(rm[i], other[rw])));
+    const float s = block_scale<QF>(amax, eps);
+    if (writes_scale && lq == 0 && col0 < N && row < M) Cs[row * ld_cs + (col0 >> 7)] = s;
+    const bool fast = scale_ok(s);
+    const float r = 1.0f / s;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rw = 16 * i + 4 * lq + e;
-      const int64_t row = row0 + rw;
-      const float amax = __uint_as_float(canon_abs_bits(max(rm[i][e], other[rw])));
-      const float s = block_scale<QF>(amax, eps);
-      if (writes_scale && lr == 0 && col0 < N && row < M) Cs[row * ld_cs + (col0 >> 7)] = s;
-      const bool fast = scale_ok(s);
-      const float r = 1.0f / s;
+    for (int j = 0; j < TJ; ++j) {
+      uint32_t w = 0;
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) {
+      for (int e = 0; e < 4; ++e) {
         const float x = acc[i][j][e];
         const uint32_t c = fast ? (cvt2<QF, false>(sat<QF>(div_rn(x, s, r)), 0.0f, 0u) & 0xFFu) : enc1<QF>(x / s);
-        // the code goes to LDS (row rw, column 16j+lr; 16-byte chunk j sits
-        // in slot j ^ ((rw >> 2) & 3))
-        stg[rw * 64 + 16 * (j ^ ((rw >> 2) & 3)) + lr] = (uint8_t)c;
+        w |= c << (8 * e);
       }
+      // four codes to LDS: row rw, columns 16j + 4lq ..; the 16-byte chunk j
+      // of a row sits in slot j ^ ((rw >> 2) & 3), so the sixteen rows of a
+      // write fall on different banks
+      *(uint32_t*)(stg + rw * 64 + 16 * (j ^ ((rw >> 2) & 3)) + 4 * lq) = w;
     }
+  }
   // The wavefront's codes leave 16 bytes per lane, four lanes per row, so
   // each row's 64 codes are written by one instruction (stored one by one
   // from the MFMA layout they left in 16-byte pieces).
@@ -305,17 +305,18 @@ __device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* l
   }
 }
 
-// C leaves through LDS.  In the 16x16 MFMA result a lane holds four rows
-// of one column, so storing straight from registers writes 32-byte (bf16)
-// or 64-byte (fp32) pieces of a row per instruction; on MI355X such partial
+// C leaves through LDS.  In the 16x16 MFMA result (operands swapped, see
+// k_gemm) a lane holds four consecutive columns of one row, so storing
+// straight from registers writes 32-byte (bf16) or 64-byte (fp32) pieces of
+// a row per instruction; on MI355X such partial
 // lines cost the memory system more than their bytes (a bf16 C stored that
 // way took longer to write than an fp32 one).  Each wavefront writes NI row
 // tiles (from row tile I0) of its TI x TJ tile into its own LDS region and
 // reads them back 16 bytes per lane, so every 64-column row piece of the
 // tile (128 bytes of bf16, 256 of fp32) leaves in one instruction.  In LDS
-// the 16-byte chunk c of row r sits in slot c ^ sw(r), chosen so that the
-// four lane groups of a write (rows 4 apart) fall on different banks and a
-// read of whole rows is conflict-free.  Columns past N are not stored;
+// the 16-byte chunk c of row r sits in slot c ^ sw(r), chosen so that a
+// write (sixteen rows, four consecutive elements per lane) takes the fewest
+// bank passes and a read of whole rows is conflict-free.  Columns past N are not stored;
 // without 16-byte aligned rows, or at a ragged right edge, the chunk is
 // stored element by element.
 template <typename T, int I0, int NI, int TI, int TJ>
@@ -324,26 +325,24 @@ __device__ __forceinline__ void store_staged(const v4f (&acc)[TI][TJ], T* stg, i
   constexpr int ES = (int)sizeof(T), EPC = 16 / ES;  // element size, elements per 16-byte chunk
   constexpr int W = TJ * 16, R = NI * 16, CH = W / EPC, RPI = 64 / CH;
   static_assert(W == 64 && (ES == 2 || ES == 4), "64-column tiles of bf16 or fp32");
-  auto sw = [](int r) { return ES == 2 ? (r >> 2) & 7 : ((r >> 2) & 3) << 2; };
+  auto sw = [](int r) { return ES == 2 ? r & 7 : (r & 3) << 2; };
   const int lr = lane & 15, lq = lane >> 4;
   __syncthreads();  // every wavefront is done with what the region held before
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
+  for (int i = 0; i < NI; ++i) {
+    const int r = 16 * i + lr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * i + 4 * lq + e;
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const int col = 16 * j + lr;
-        const float v = acc[I0 + i][j][e];
-        T t;
-        if constexpr (ES == 2)
-          t = (T)f32_to_bf16(v);
-        else
-          t = v;
-        stg[r * W + EPC * ((col / EPC) ^ sw(r)) + col % EPC] = t;
-      }
+    for (int j = 0; j < TJ; ++j) {
+      // columns 16j + 4lq .. +3 of row r: four consecutive elements
+      const v4f v = acc[I0 + i][j];
+      const int col = 16 * j + 4 * lq;
+      T* d = stg + r * W + EPC * ((col / EPC) ^ sw(r)) + col % EPC;
+      if constexpr (ES == 2)
+        *(u32x2*)d = u32x2{f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+      else
+        *(v4f*)d = v;
     }
+  }
   __syncthreads();
   const bool vec = (((uintptr_t)C | (uintptr_t)(ldc * ES)) & 15) == 0;
   const int rr = lane / CH, c = lane % CH;
@@ -419,8 +418,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
 
   // A scales: wavefront w stages rows w*BM/8 .. +BM/8 of the tile, one per
   // lane (rows past M read the last row)
+  // In LDS the scales are ordered so that the TI scales one lane needs
+  // (rows 16i + lr of its wavefront half, i = 0..TI-1) are contiguous: slot
+  // p = h*16TI + lr*TI + i holds row h*16TI + 16i + lr.
   constexpr int SA_LANES = BM / 8;
-  const int64_t sa_r = m0 + wave * SA_LANES + (lane < SA_LANES ? lane : 0);
+  const int sa_p = wave * SA_LANES + (lane < SA_LANES ? lane : 0);
+  const int64_t sa_r = m0 + (sa_p / (16 * TI)) * 16 * TI + 16 * (sa_p % TI) + (sa_p % (16 * TI)) / TI;
   const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
   uint32_t a_off[BM / 64], b_off[BN / 64];
   dma_offsets<BM>(a_off, lda, m0, M, wave, lane);
@@ -445,35 +448,52 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);
   const float* sb_col = sB + (sb_c < N ? sb_c : N - 1) * sB_sn;
 
-  // P_kb of every MFMA tile of the wavefront, folded into acc
+  // P_kb of every MFMA tile of the wavefront, folded into acc.  The MFMAs
+  // take the B fragment as their first operand and the A fragment as their
+  // second, so a 16x16 result holds C transposed: lane (lr, lq) gets row
+  // 16i + lr and columns 16j + 4lq + e.  A lane then needs one A scale per
+  // row tile (not four), and its four results of a tile are consecutive
+  // columns of one row.
   auto compute = [&](int64_t kb, int s) {
     // the B scale(s) of this wavefront's columns
-    float sbv[TJ];
+    v4f sbv[TJ];
     float sbw = 1.0f;
     if constexpr (GB == FP8Q_GRAN_128x128) {
       sbw = sb_blk[kb * sB_skb];
     } else {
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) sbv[j] = lds_sb[s][wn * TJ * 16 + 16 * j + lr];
+      for (int j = 0; j < TJ; ++j) {
+        const float4 t = *(const float4*)(lds_sb[s] + wn * TJ * 16 + 16 * j + 4 * lq);
+        sbv[j] = v4f{t.x, t.y, t.z, t.w};
+      }
     }
     const uint8_t* la = lds_a[s] + a_row0;
     const uint8_t* lb = lds_b[s] + b_row0;
-    const float* lc = lds_sa[s] + wm * TI * 16 + 4 * lq;
-    auto coef = [&](int i) {
-      const float4 c4 = *(const float4*)(lc + 16 * i);
-      v4f c = {c4.x, c4.y, c4.z, c4.w};
-      if constexpr (GB == FP8Q_GRAN_128x128) c = c * sbw;
-      return c;
-    };
+    // the lane's TI A scales (times the block's B scale with 128x128 B scales)
+    float cf[TI];
+    {
+      const float* lc = lds_sa[s] + wm * TI * 16 + lr * TI;
+#pragma unroll
+      for (int q = 0; q < TI / 4; ++q) {
+        const float4 c4 = *(const float4*)(lc + 4 * q);
+        cf[4 * q] = c4.x;
+        cf[4 * q + 1] = c4.y;
+        cf[4 * q + 2] = c4.z;
+        cf[4 * q + 3] = c4.w;
+      }
+      if constexpr (GB == FP8Q_GRAN_128x128) {
+#pragma unroll
+        for (int i = 0; i < TI; ++i) cf[i] = cf[i] * sbw;
+      }
+    }
     // one promotion FMA: acc[i][j][e] += P * (sA * sB)
-    auto fold = [&](int i, int j, int e, float p, const v4f& c) {
+    auto fold = [&](int i, int j, int e, float p) {
       if constexpr (GB == FP8Q_GRAN_128x128)
-        acc[i][j][e] = __builtin_fmaf(p, c[e], acc[i][j][e]);
+        acc[i][j][e] = __builtin_fmaf(p, cf[i], acc[i][j][e]);
       else
-        acc[i][j][e] = __builtin_fmaf(p * c[e], sbv[j], acc[i][j][e]);
+        acc[i][j][e] = __builtin_fmaf(p * cf[i], sbv[j][e], acc[i][j][e]);
     };
     v4f pp[TJ], pn[TJ];
-    v4f cp = {0.0f, 0.0f, 0.0f, 0.0f}, cc = coef(0);
     if constexpr (FAST) {
       // 16x16x128: the lane holds logical chunks 2q, 2q+1 (q = l/16) of its row
       const int o0 = 16 * swz_chunk(lr, 2 * lq), o1 = 16 * swz_chunk(lr, 2 * lq + 1);
@@ -488,27 +508,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
       v8i fa = frag(la), fn = fa;
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
-        v4f cn = cc;
-        if (i + 1 < TI) {
-          fn = frag(la + 16 * (i + 1) * BK);
-          cn = coef(i + 1);
-        }
+        if (i + 1 < TI) fn = frag(la + 16 * (i + 1) * BK);
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], v4f{0.0f, 0.0f, 0.0f, 0.0f}, FA,
-                                                                  FB, 0, 0, 0, 0);
+          pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, v4f{0.0f, 0.0f, 0.0f, 0.0f}, FB,
+                                                                  FA, 0, 0, 0, 0);
           pin(pn[j]);
           if (i > 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) fold(i - 1, j, e, pp[j][e], cp);
+            for (int e = 0; e < 4; ++e) fold(i - 1, j, e, pp[j][e]);
             pin(acc[i - 1][j]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
-        cp = cc;
-        cc = cn;
         fa = fn;
       }
     } else {
@@ -548,20 +562,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
 #pragma unroll
       for (int i = 0; i < TI; ++i) {
         u32x2 raw[4];
-        v4f cn = cc;
-        if (i + 1 < TI) {
-          raw32(la + 16 * (i + 1) * BK, raw);
-          cn = coef(i + 1);
-        }
+        if (i + 1 < TI) raw32(la + 16 * (i + 1) * BK, raw);
         V2 part[4][4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
-            pn[j] = mfma16x32<H16>(fa[kk], fb[j][kk], kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j]);
+            pn[j] = mfma16x32<H16>(fb[j][kk], fa[kk], kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j]);
             pin(pn[j]);
             if (i > 0) {
-              fold(i - 1, j, kk, pp[j][kk], cp);
+              fold(i - 1, j, kk, pp[j][kk]);
               pin(acc[i - 1][j]);
             }
             if (i + 1 < TI) {
@@ -585,15 +595,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
         }
 #pragma unroll
         for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
-        cp = cc;
-        cc = cn;
       }
     }
     // the last row tile's promotion
 #pragma unroll
     for (int j = 0; j < TJ; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) fold(TI - 1, j, e, pp[j][e], cp);
+      for (int e = 0; e < 4; ++e) fold(TI - 1, j, e, pp[j][e]);
   };
 
   // Everything one wavefront copies into LDS stage st for K block kb.
@@ -745,7 +753,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
       const int sai = lds_sa[st][(a_row0 + 16 * i) * 4 + lq];
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fa, fb[j], acc[i][j], FA, FB, 0, sai, 0, sbj[j]);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, acc[i][j], FB, FA, 0, sbj[j], 0, sai);
     }
   };
 
