@@ -32,6 +32,8 @@
 // tile grid.
 #include "fp8q_internal.h"
 
+#include <type_traits>
+
 namespace fp8q {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -732,44 +734,78 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
     lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
   };
 
-  auto compute = [&](int st) {
-    const uint8_t* la = lds_a[st] + a_row0 * BK;
-    const uint8_t* lb = lds_b[st] + b_row0 * BK;
-    auto frag = [&](const uint8_t* base) {
-      const u32x4 x0 = *(const u32x4*)(base + o0);
-      const u32x4 x1 = *(const u32x4*)(base + o1);
-      return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    };
-    v8i fb[TJ];
-    int sbj[TJ];
+  auto frag = [&](const uint8_t* base) {
+    const u32x4 x0 = *(const u32x4*)(base + o0);
+    const u32x4 x1 = *(const u32x4*)(base + o1);
+    return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  };
+  // B fragments and scales of the block being computed; A fragments and
+  // scales of two row tiles (the one computed and the next), by parity.
+  // Per stage, a lane reads at fixed offsets from four bases.
+  v8i fb[TJ], fa[2];
+  int sbj[TJ], sai[2];
+  auto load_b = [&](int st, int j) {
+    const uint8_t* lb = &lds_b[0][0] + st * (BN * BK) + b_row0 * BK + 16 * j * BK;
+    const u32x4 x0 = *(const u32x4*)(lb + o0);
+    const u32x4 x1 = *(const u32x4*)(lb + o1);
+    fb[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    sbj[j] = (&lds_sb[0][0])[st * (BN * 4) + (b_row0 + 16 * j) * 4 + lq];
+  };
+  auto load_a = [&](int st, int i) {
+    const uint8_t* la = &lds_a[0][0] + st * (BM * BK) + a_row0 * BK + 16 * i * BK;
+    const u32x4 x0 = *(const u32x4*)(la + o0);
+    const u32x4 x1 = *(const u32x4*)(la + o1);
+    fa[i & 1] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    sai[i & 1] = (&lds_sa[0][0])[st * (BM * 4) + (a_row0 + 16 * i) * 4 + lq];
+  };
+  auto mma = [&](int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i & 1], acc[i][j], FB, FA, 0, sbj[j], 0,
+                                                                sai[i & 1]);
+  };
+  // row tiles 0 .. TI-2 of a block, each with the next row tile's A read
+  auto rows = [&](int st) {
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      fb[j] = frag(lb + 16 * j * BK);
-      sbj[j] = lds_sb[st][(b_row0 + 16 * j) * 4 + lq];
-    }
+    for (int i = 0; i + 1 < TI; ++i) {
+      load_a(st, i + 1);
 #pragma unroll
-    for (int i = 0; i < TI; ++i) {
-      const v8i fa = frag(la + 16 * i * BK);
-      const int sai = lds_sa[st][(a_row0 + 16 * i) * 4 + lq];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, acc[i][j], FB, FA, 0, sbj[j], 0, sai);
+      for (int j = 0; j < TJ; ++j) mma(i, j);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
+  static_assert(TI % 2 == 0, "row tile 0 of every block uses A slot 0");
 
+  // Software pipeline over K blocks (two LDS stages, block kb in stage
+  // kb % 2).  The barrier that publishes block kb sits before the last row
+  // tile of block kb-1; right after it the copy of block kb+1 goes into the
+  // stage block kb-1 has finished with, and the fragments of block kb are
+  // read behind the last row tile's MFMAs, so no block starts by waiting
+  // for its first LDS reads.  One pass of the loop is the last row tile of
+  // block kb-1 followed by the other row tiles of block kb.
   stage_block(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  int st = 0;
-  int64_t kb = 0;
-  for (; kb + 1 < nkb; ++kb) {
-    stage_block(kb + 1, st ^ 1);
-    compute(st);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (nkb > 1) stage_block(1, 1);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) load_b(0, j);
+  load_a(0, 0);
+  rows(0);
+  for (int64_t kb = 1; kb < nkb; ++kb) {
+    const int st = (int)(kb & 1);
+    // every lane's reads of stage st^1 are done and block kb has landed
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    st ^= 1;
+    if (kb + 1 < nkb) stage_block(kb + 1, st ^ 1);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      mma(TI - 1, j);
+      load_b(st, j);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    load_a(st, 0);
+    rows(st);
   }
-  compute(st);
+#pragma unroll
+  for (int j = 0; j < TJ; ++j) mma(TI - 1, j);
 
   // ---- epilogue
   constexpr int WB = TI * 16 * TJ * 16 * 2;
