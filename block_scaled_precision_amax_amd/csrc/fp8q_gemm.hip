@@ -22,13 +22,16 @@
 //     128 block (the situation the handbook's promotion rule is written for).
 //
 // Tiling: a 256x256 output tile per workgroup of eight wavefronts (2x4,
-// each 128x64 = 8x4 MFMA tiles of 16x16).  Per 128-wide K block the A and B
-// code tiles (32 KB each) are copied into LDS by the global-to-LDS load
-// path, double buffered and one block ahead, with an XOR chunk swizzle that
-// keeps the fragment reads free of bank conflicts.  The per-row promotion
-// coefficient sA*sB of the tile's 256 rows travels with the codes, so
-// promotion is one FMA per output element and K block.  Workgroups are renumbered so that each of
-// the eight XCDs (one L2 each) walks a contiguous, M-grouped part of the
+// each 128x64 = 8x4 MFMA tiles of 16x16) on the FP8 paths, 128x256 (each
+// wavefront 64x64) on the exact path.  Per 128-wide K block the A and B
+// code tiles are copied into LDS by the global-to-LDS load path (two stages
+// on the FP8 paths, three on the exact path), with an XOR chunk swizzle
+// that keeps the fragment reads free of bank conflicts.  The A scales of
+// the tile's rows travel with the codes, so promotion is one FMA per output
+// element and K block.  The MFMAs take B as their first operand, so each
+// lane holds one row and four consecutive columns of C, and C leaves
+// through LDS in whole row pieces.  Workgroups are renumbered so that each
+// of the eight XCDs (one L2 each) walks a contiguous, M-grouped part of the
 // tile grid.
 #include "fp8q_internal.h"
 
