@@ -376,7 +376,28 @@ def cpu_baseline(inputs, budget_s: float = 20.0):
         rows_g = hi
         chunk *= 2
     est = (t_ds * n / m_ds + t_q * LM / rows_x + t_g * LM / rows_g)
-    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    cores = orc.max_threads()
+    # the same on one thread, on a smaller sample (a few seconds)
+    orc.set_threads(1)
+    try:
+        r1 = 128
+        t0 = time.perf_counter()
+        q1 = orc.quantize_tensor(xs[:r1], orc.E4M3FN, 0.05)
+        orc.quantize_tensor(gs[:r1], orc.E5M2, 1e-6)
+        orc.amax(xs[:r1])
+        orc.amax(gs[:r1])
+        orc.dequantize(q1.reshape(1, -1), orc.E4M3FN, np.array([0.05], np.float32), orc.GRAN_TENSOR, out_bf16=True)
+        t1_ds = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        qa1, sa1 = orc.quantize_1x128(Xs[:r1], orc.E4M3FN)
+        t1_q = time.perf_counter() - t0
+        g1 = 4
+        t0 = time.perf_counter()
+        orc.gemm_blockscaled(qa1[:g1], orc.E4M3FN, sa1[:g1], qW, orc.E4M3FN, sW, orc.GRAN_128x128)
+        t1_g = time.perf_counter() - t0
+    finally:
+        orc.set_threads(cores)
+    est1 = t1_ds * n / (r1 * DS_COLS) + t1_q * LM / r1 + t1_g * LM / g1
     return {
         "value": alg["gemm_flop"] / est / 1e12,
         "unit": "TFLOP/s",
@@ -386,6 +407,10 @@ def cpu_baseline(inputs, budget_s: float = 20.0):
                    f"dequantize), {rows_x} of {LM} activation rows (1x128 quantize) and {rows_g} of {LM} "
                    f"GEMM rows; measured {t_ds + t_q + t_g:.1f} s, extrapolated per element / per row "
                    f"to a full step of {est:.1f} s"),
+        "single_thread": {"value": alg["gemm_flop"] / est1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                          "sample": (f"{r1} rows of each delayed-scaling tensor, {r1} activation rows and "
+                                     f"{g1} GEMM rows on one thread; measured {t1_ds + t1_q + t1_g:.1f} s, "
+                                     f"extrapolated to a full step of {est1:.0f} s")},
     }
 
 

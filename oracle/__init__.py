@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         vp, i64, i32, f32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_uint32
         sig = {
             "orc_max_finite": (ctypes.c_double, [i32]),
+            "orc_set_threads": (None, [i32]),
+            "orc_max_threads": (i32, []),
             "orc_decode": (ctypes.c_double, [u32, i32]),
             "orc_encode": (u32, [f32, i32]),
             "orc_encode_array": (None, [vp, i64, i32, vp]),
@@ -97,6 +99,15 @@ def _dtype_code(x: np.ndarray) -> int:
 
 
 # ---------------------------------------------------------------- codec
+def set_threads(n: int) -> None:
+    """OpenMP threads the oracle's loops use (timing only; results do not depend on it)."""
+    lib().orc_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
 def decode(code: int, fmt: int) -> float:
     return lib().orc_decode(int(code) & 0xFF, fmt)
 

@@ -518,3 +518,9 @@ void orc_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64
 }
 
 int orc_version(void) { return 1; }
+
+/* Thread count of the OpenMP loops above (timing of the oracle on one core
+ * beside all cores); the results do not depend on it. */
+#include <omp.h>
+void orc_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int orc_max_threads(void) { return omp_get_max_threads(); }
