@@ -779,11 +779,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
     lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
   };
 
-  auto frag = [&](const uint8_t* base) {
-    const u32x4 x0 = *(const u32x4*)(base + o0);
-    const u32x4 x1 = *(const u32x4*)(base + o1);
-    return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-  };
   // B fragments and scales of the block being computed; A fragments and
   // scales of two row tiles (the one computed and the next), by parity.
   // Per stage, a lane reads at fixed offsets from four bases.
