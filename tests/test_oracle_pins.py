@@ -276,6 +276,134 @@ def test_outlier_experiment_other_seeds(orc):
         assert prev > 0.10
 
 
+# ------------------------------------------------------------------ the handbook's formula in torch
+# Handbook "FP8 训练": quantizing is dividing by the dequantization scale in
+# float32, clamping to +-MAX and casting to float8; the per-tensor scale is
+# the tensor's amax over MAX, the per-block scale the block's amax, clamped
+# below at 1e-12, over MAX.  Written here with torch's own CPU float32
+# arithmetic (IEEE division) and its RNE float8 cast, independently of the
+# oracle, and compared code for code and scale for scale.  NaN is left out:
+# torch's cast keeps a NaN's sign, the reading here maps every NaN to 0x7F.
+def _torch_codes(x, s, fmt):
+    """(x / s) in float32, clamped to +-MAX, cast to float8: the code bytes."""
+    return (x / s).clamp(-MAXF[fmt], MAXF[fmt]).to(TORCH_FP8[fmt]).view(torch.uint8)
+
+
+def _torch_per_tensor(x, fmt):
+    s = x.abs().max() / MAXF[fmt]
+    return _torch_codes(x, s, fmt), s
+
+
+def _torch_per_block(x, rows, cols, fmt):
+    R, C = x.shape
+    b = x.reshape(R // rows, rows, C // cols, cols)
+    s = b.abs().amax(dim=(1, 3), keepdim=True).clamp(min=1e-12) / MAXF[fmt]
+    q = _torch_codes(b, s, fmt).reshape(R, C)
+    return q, s.reshape(R // rows, C // cols)
+
+
+def _as_np(t):
+    return t.contiguous().numpy()
+
+
+def test_handbook_formula_outlier_tensors(orc):
+    """The printed experiment's tensors (seed 0, columns 0-3 scaled by 1e2,
+    1e4, 3e4): per-tensor and 1x128 codes and scales of the oracle equal the
+    handbook's formula evaluated by torch, bit for bit, in both formats."""
+    g = golden("outlier_experiment.json")
+    torch.manual_seed(g["seed"])
+    for f in g["factors"]:
+        a = torch.randn(*g["shape"])
+        a[:, : g["outlier_cols"]] *= f
+        x = a.numpy()
+        for fmt in (E4, E5):
+            qt, st = _torch_per_tensor(a, fmt)
+            s = orc.scale(orc.amax(x), fmt)
+            assert np.float32(st.item()) == s
+            assert np.array_equal(orc.quantize_tensor(x, fmt, s), _as_np(qt)), (f, fmt)
+            for br, bc in ((1, 128), (128, 128)):
+                qb, sb = _torch_per_block(a, br, bc, fmt)
+                oq, os_ = orc.quantize_blocks(x, br, bc, fmt)
+                assert np.array_equal(os_, _as_np(sb)), (f, fmt, br)
+                assert np.array_equal(oq, _as_np(qb)), (f, fmt, br)
+
+
+# per-tensor scales across regimes: ordinary non-powers of two, a scale whose
+# reciprocal is far from exact, tiny (fp32 subnormal) and huge scales, and one
+# where quotients land on FP8 rounding midpoints
+_SCALE_REGIMES = [0.0173, 1.0 / 3.0, 11.160714149475098, 7.0e-3, 3.3e-39, 1.7e-42, 2.9e35, 0.5, 1.0]
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_handbook_formula_scale_regimes(orc, fmt, dtype):
+    """Random fp32 / bf16 data (magnitudes over many octaves, NaN removed)
+    quantized with a given per-tensor scale: oracle codes == torch's
+    float32 (x / s).clamp(-MAX, MAX).to(float8), for every scale regime."""
+    rng = np.random.default_rng(11)
+    for s in _SCALE_REGIMES:
+        s32 = np.float32(s)
+        base = rng.standard_normal(1 << 16) * np.exp2(rng.uniform(-30, 30, 1 << 16))
+        x = (base * float(s32) * MAXF[fmt] / 64.0).astype(np.float32)
+        # quotients exactly on rounding midpoints of the format, and +-0
+        mids = (np.arange(1, 200, dtype=np.float32) * np.float32(2.0 ** -10)) * s32
+        x = np.concatenate([x, mids, -mids, np.float32([0.0, -0.0])])
+        x = x[np.isfinite(x) | np.isinf(x)]
+        if dtype == "bf16":
+            xt = torch.from_numpy(x).to(torch.bfloat16)
+            xin = xt.view(torch.int16).numpy().view(np.uint16)
+            xt = xt.float()
+        else:
+            xt = torch.from_numpy(x)
+            xin = x
+        ref = _as_np(_torch_codes(xt, torch.tensor(s32), fmt))
+        assert np.array_equal(orc.quantize_tensor(xin, fmt, s32), ref), s
+
+
+def _midpoints(fmt):
+    """Every point halfway between two neighbouring non-negative finite
+    values of the format (from its bit layout: bias 7 / 15, 3 / 2 mantissa
+    bits), as fp64."""
+    M, bias, emax = (3, 7, 15) if fmt == E4 else (2, 15, 30)
+    vals = [m * 2.0 ** (1 - bias - M) for m in range(1 << M)]
+    for e in range(1, emax + 1):
+        vals += [(1 + m / 2 ** M) * 2.0 ** (e - bias) for m in range(1 << M)]
+    v = np.array([t for t in vals if t <= MAXF[fmt]])
+    return (v[:-1] + v[1:]) / 2
+
+
+def test_quotient_is_correctly_rounded_float32(orc):
+    """The quotient step q = enc(fl32(x / s)) against (float)((double)x /
+    (double)s): rounding the double quotient once more to fp32 is the
+    correctly rounded fp32 quotient (53 >= 2*24 + 2: double rounding of a
+    quotient is innocuous, Figueroa 1995).  Checked through the codes on a
+    large random sample of (x, s) pairs, including every exponent range."""
+    rng = np.random.default_rng(12)
+    ns, per = 256, 1 << 12
+    # scales from fp32 subnormals to 2^100, every mantissa; random fp32 data
+    sb = rng.integers(0x00000001, 0x71800000, size=ns, dtype=np.uint64).astype(np.uint32)
+    scales = sb.view(np.float32)
+    for fmt in (E4, E5):
+        for i, v in enumerate(scales):
+            xb = rng.integers(0, 1 << 32, size=per, dtype=np.uint64).astype(np.uint32)
+            x = xb.view(np.float32)
+            # half of the data near the scale, where the codes are not all 0 or MAX
+            x[: per // 2] = (rng.standard_normal(per // 2) * float(v) * 64.0).astype(np.float32)
+            # and values whose quotients lie on or next to the format's rounding
+            # midpoints, where one ulp of the quotient decides the code
+            mids = _midpoints(fmt)
+            near = (mids * np.float64(v)).astype(np.float32)
+            near = np.concatenate([np.nextafter(near, np.float32(np.inf)), near, np.nextafter(near, np.float32(0))])
+            x = np.concatenate([x, near, -near])
+            x = x[~np.isnan(x)]
+            y = (x.astype(np.float64) / np.float64(v)).astype(np.float32)
+            want = orc.encode_array(y, fmt)
+            assert np.array_equal(orc.quantize_tensor(x, fmt, v), want), (fmt, float(v))
+            if i < 4:
+                got = np.array([orc.quantize_value(float(a), float(v), fmt) for a in x[:512]], dtype=np.uint8)
+                assert np.array_equal(got, want[:512])
+
+
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("br,bc", [(1, 128), (128, 128)])
 def test_block_quantize_invariants(orc, fmt, br, bc):
