@@ -44,6 +44,7 @@ SYMBOLS = (
     "fp8q_gemm_mx",
     "fp8q_gemm_blockscaled_q",
     "fp8q_quantize_tensor_dq",
+    "fp8q_quantize_tensor_delayed",
 )
 
 
@@ -59,7 +60,7 @@ class Scaler(ctypes.Structure):
     _fields_ = [("ring", ctypes.c_float * 1024), ("window", ctypes.c_int32), ("count", ctypes.c_int32),
                 ("pos", ctypes.c_int32), ("max_val", ctypes.c_float), ("eps", ctypes.c_float),
                 ("margin", ctypes.c_float), ("scale", ctypes.c_float), ("stat", ctypes.c_int32),
-                ("alpha", ctypes.c_float), ("reserved", ctypes.c_int32), ("ema", ctypes.c_double)]
+                ("alpha", ctypes.c_float), ("amax_acc", ctypes.c_float), ("ema", ctypes.c_double)]
 
 
 STAT_MAX, STAT_MEAN, STAT_EMA = 0, 1, 2
@@ -101,6 +102,7 @@ def lib() -> ctypes.CDLL:
                                                  vp, i32, i64, i64, i64, i64, vp]),
             "fp8q_gemm_mx": (i32, [vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp, i32, i64, i64, i64, i64, vp]),
             "fp8q_quantize_tensor_dq": (i32, [vp, i32, i64, i32, vp, vp, vp, vp, i32, vp]),
+            "fp8q_quantize_tensor_delayed": (i32, [vp, i32, i64, i32, vp, vp, vp, i32, vp]),
             "fp8q_gemm_blockscaled_q": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64, i32, f32,
                                               vp, i64, vp, i64, i64, i64, i64, vp]),
         }
@@ -154,8 +156,8 @@ def fp8q_amax(x, n, amax, stream=None) -> None:
     _check(lib().fp8q_amax(_ptr(x), _dt(x), n, _ptr(amax), _stream(stream, x)))
 
 
-def fp8q_quantize_tensor(x, n, f, scale, q, amax_acc=None, stream=None) -> None:
-    _check(lib().fp8q_quantize_tensor(_ptr(x), _dt(x), n, f, _ptr(scale), _ptr(q), _ptr(amax_acc),
+def fp8q_quantize_tensor(x, n, f, scale, q, amax_out=None, stream=None) -> None:
+    _check(lib().fp8q_quantize_tensor(_ptr(x), _dt(x), n, f, _ptr(scale), _ptr(q), _ptr(amax_out),
                                       _stream(stream, x)))
 
 
@@ -193,7 +195,7 @@ def fp8q_delayed_scaler_init_stat(state, window, max_val, eps, margin, stat, alp
                                                _stream(stream, state)))
 
 
-def fp8q_delayed_scaler_update(state, amax, stream=None) -> None:
+def fp8q_delayed_scaler_update(state, amax=None, stream=None) -> None:
     _check(lib().fp8q_delayed_scaler_update(_ptr(state), _ptr(amax), _stream(stream, state)))
 
 
@@ -227,6 +229,11 @@ def fp8q_gemm_blockscaled_q(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb, s
                                          _stream(stream, A)))
 
 
-def fp8q_quantize_tensor_dq(x, n, f, scale, q, y, amax_acc=None, stream=None) -> None:
-    _check(lib().fp8q_quantize_tensor_dq(_ptr(x), _dt(x), n, f, _ptr(scale), _ptr(q), _ptr(amax_acc), _ptr(y),
+def fp8q_quantize_tensor_dq(x, n, f, scale, q, y, amax_out=None, stream=None) -> None:
+    _check(lib().fp8q_quantize_tensor_dq(_ptr(x), _dt(x), n, f, _ptr(scale), _ptr(q), _ptr(amax_out), _ptr(y),
                                          _dt(y), _stream(stream, x)))
+
+
+def fp8q_quantize_tensor_delayed(x, n, f, state, q, y=None, stream=None) -> None:
+    _check(lib().fp8q_quantize_tensor_delayed(_ptr(x), _dt(x), n, f, _ptr(state), _ptr(q), _ptr(y),
+                                              _dt(y) if y is not None else F32, _stream(stream, x)))

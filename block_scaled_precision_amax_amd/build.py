@@ -1,4 +1,6 @@
-"""Builds libfp8q.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Builds libfp8q.so (the HIP kernels and the C ABI) for gfx950 with hipcc,
+and libfp8q_stream.so, the streaming-bandwidth reference the benchmark sets
+the quantizers against (not part of the library's ABI).
 
 Each csrc/*.hip is compiled to an object in parallel, then linked into the
 package directory, where the Python binding loads it.  Flags:
@@ -17,9 +19,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libfp8q.so")
+STREAM_LIB = os.path.join(HERE, "libfp8q_stream.so")
 ARCH = os.environ.get("FP8Q_ARCH", "gfx950")
 
 SOURCES = ["fp8q_api.hip", "fp8q_quant.hip", "fp8q_gemm.hip"]
+STREAM_SOURCES = ["fp8q_stream.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}",
@@ -50,20 +54,27 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(extra: list[str] | None = None, save_temps: bool = False) -> str:
-    """Compile every HIP source and link libfp8q.so.  Always recompiles."""
-    os.makedirs(BUILD, exist_ok=True)
-    extra = list(extra or [])
-    if save_temps:
-        extra += ["-save-temps=obj"]
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra: list[str] | None = None, save_temps: bool = False) -> str:
+    """Compile every HIP source and link libfp8q.so and libfp8q_stream.so.
+    Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    extra = list(extra or [])
+    if save_temps:
+        extra += ["-save-temps=obj"]
+    srcs = SOURCES + STREAM_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, extra), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], STREAM_LIB)
     return LIB
 
 

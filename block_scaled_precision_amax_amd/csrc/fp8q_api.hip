@@ -102,25 +102,38 @@ int fp8q_amax(const void* x, fp8q_dtype dt, int64_t n, float* amax, void* stream
 }
 
 int fp8q_quantize_tensor(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
-                         uint8_t* q, float* amax_acc, void* stream) {
+                         uint8_t* q, float* amax_out, void* stream) {
   if (!x || !scale || !q) return fail(FP8Q_EINVAL, "quantize_tensor: null pointer");
   if (!valid_dt(dt) || !valid_fmt(f)) return fail(FP8Q_EINVAL, "quantize_tensor: bad dtype or format");
   if (n <= 0) return fail(FP8Q_EINVAL, "quantize_tensor: n must be positive");
-  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || (amax_acc && !aligned(amax_acc, 4)))
+  if (!aligned(x, 16) || !aligned(q, 16) || !aligned(scale, 4) || (amax_out && !aligned(amax_out, 4)))
     return fail(FP8Q_EALIGN, "quantize_tensor: x and q must be 16-byte aligned");
-  return launch_quantize_tensor(x, dt, n, f, scale, q, amax_acc, S(stream));
+  return launch_quantize_tensor(x, dt, n, f, scale, q, amax_out, true, S(stream));
 }
 
 int fp8q_quantize_tensor_dq(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
-                            uint8_t* q, float* amax_acc, void* y, fp8q_dtype out_dt, void* stream) {
+                            uint8_t* q, float* amax_out, void* y, fp8q_dtype out_dt, void* stream) {
   if (!x || !scale || !q || !y) return fail(FP8Q_EINVAL, "quantize_tensor_dq: null pointer");
   if (!valid_dt(dt) || !valid_fmt(f) || !valid_dt(out_dt))
     return fail(FP8Q_EINVAL, "quantize_tensor_dq: bad dtype or format");
   if (n <= 0) return fail(FP8Q_EINVAL, "quantize_tensor_dq: n must be positive");
   if (!aligned(x, 16) || !aligned(q, 16) || !aligned(y, 16) || !aligned(scale, 4) ||
-      (amax_acc && !aligned(amax_acc, 4)))
+      (amax_out && !aligned(amax_out, 4)))
     return fail(FP8Q_EALIGN, "quantize_tensor_dq: x, q and y must be 16-byte aligned");
-  return launch_quantize_tensor(x, dt, n, f, scale, q, amax_acc, S(stream), y, out_dt);
+  return launch_quantize_tensor(x, dt, n, f, scale, q, amax_out, true, S(stream), y, out_dt);
+}
+
+int fp8q_quantize_tensor_delayed(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, fp8q_scaler* state,
+                                 uint8_t* q, void* y, fp8q_dtype out_dt, void* stream) {
+  if (!x || !state || !q) return fail(FP8Q_EINVAL, "quantize_tensor_delayed: null pointer");
+  if (!valid_dt(dt) || !valid_fmt(f) || (y && !valid_dt(out_dt)))
+    return fail(FP8Q_EINVAL, "quantize_tensor_delayed: bad dtype or format");
+  if (n <= 0) return fail(FP8Q_EINVAL, "quantize_tensor_delayed: n must be positive");
+  if (!aligned(x, 16) || !aligned(q, 16) || (y && !aligned(y, 16)) || !aligned(state, 8))
+    return fail(FP8Q_EALIGN, "quantize_tensor_delayed: x, q and y must be 16-byte aligned, state 8-byte");
+  // the scale in force and the step's running amax live in the state
+  return launch_quantize_tensor(x, dt, n, f, &state->scale, q, &state->amax_acc, false, S(stream), y,
+                                y ? (int)out_dt : -1);
 }
 
 int fp8q_quantize_1x128(const void* x, fp8q_dtype dt, int64_t rows, int64_t cols, int64_t ldx,
@@ -208,7 +221,8 @@ int fp8q_delayed_scaler_init(fp8q_scaler* state, int32_t window, float max_val, 
 }
 
 int fp8q_delayed_scaler_update(fp8q_scaler* state, float* amax, void* stream) {
-  if (!state || !amax) return fail(FP8Q_EINVAL, "delayed_scaler_update: null pointer");
+  if (!state) return fail(FP8Q_EINVAL, "delayed_scaler_update: null pointer");
+  if (!amax) amax = &state->amax_acc;  // the step's amax folded in by quantize_tensor_delayed
   if (!aligned(state, 8) || !aligned(amax, 4))
     return fail(FP8Q_EALIGN, "delayed_scaler_update: state must be 8-byte and amax 4-byte aligned");
   return launch_scaler_update(state, amax, S(stream));

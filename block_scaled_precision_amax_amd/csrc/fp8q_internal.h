@@ -133,8 +133,10 @@ FP8Q_DEV uint32_t wave_max(uint32_t v) {
 
 // ---------------------------------------------------------------- launches
 int launch_amax(const void* x, int dt, int64_t n, float* amax, hipStream_t st);
+// amax (nullable) gets max|x|: overwritten when reset_amax (a one-thread
+// reset launch precedes the pass), folded in as a running maximum otherwise.
 int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const float* scale, uint8_t* q,
-                           float* amax_acc, hipStream_t st, void* y = nullptr, int out_dt = -1);
+                           float* amax, bool reset_amax, hipStream_t st, void* y = nullptr, int out_dt = -1);
 int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                           float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                           hipStream_t st);

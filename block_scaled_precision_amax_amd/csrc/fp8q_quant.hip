@@ -35,14 +35,6 @@ __device__ __forceinline__ uint32_t pk_fold(uint32_t acc) {
   return max(acc & 0xFFFFu, acc >> 16) << 16;
 }
 
-// Folds a workgroup's maximum into *p.  The accumulator only grows, so a
-// workgroup whose maximum does not exceed the value already there skips the
-// atomic: one relaxed read instead of an atomic per workgroup, which
-// otherwise serialize on the one address.
-__device__ __forceinline__ void fold_max(uint32_t* p, uint32_t m) {
-  if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
-}
-
 // Workgroup-wide maximum of one value per thread (kThreads threads).
 __device__ __forceinline__ uint32_t block_max(uint32_t v) {
   __shared__ uint32_t part[kThreads / 64];
@@ -56,6 +48,17 @@ __device__ __forceinline__ uint32_t block_max(uint32_t v) {
   return m;
 }
 
+// Folds a workgroup's maximum into *p (a running maximum on the bit pattern;
+// non-negative floats order like their bit patterns, NaN patterns above
+// +Inf).  The value only grows, so a workgroup whose maximum does not exceed
+// the one already there skips the atomic: one relaxed read instead of an
+// atomic per workgroup (same-address atomics serialize, tens of
+// nanoseconds each on this chip).
+__device__ __forceinline__ void fold_max(uint32_t* p, uint32_t m) {
+  if (m > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, m);
+}
+
+// The reset of an output that a reduction then folds into.
 __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 
 // ---------------------------------------------------------------- amax
@@ -139,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void k_amax(const void* __restrict__ x, i
 // ---------------------------------------------------------------- per-tensor
 // Quantize with the scale at *scale (read on the device), folding max|x|
 // into *amax_acc when given.  The fast path divides with div_rn_wide; a
-// vector holding a NaN re-encodes its elements one by one (NaN -> 0x7F),
-// and a scale outside [2^-80, 2^80] (or NaN / zero / Inf) takes IEEE
-// division for every element.
+// vector holding a NaN re-encodes its
+// elements one by one (NaN -> 0x7F), and a scale outside [2^-80, 2^80] (or
+// NaN / zero / Inf) takes IEEE division for every element.
 template <int FMT>
 __device__ __forceinline__ uint32_t quant4_fast(float a, float b, float c, float d, float s, float r) {
   return pack4<FMT>(sat<FMT>(div_rn_wide(a, s, r)), sat<FMT>(div_rn_wide(b, s, r)),
@@ -573,7 +576,7 @@ __global__ void k_scaler_init(fp8q_scaler* st, int32_t window, float max_val, fl
     st->scale = 1.0f;
     st->stat = stat;
     st->alpha = alpha;
-    st->reserved = 0;
+    st->amax_acc = 0.0f;
     st->ema = 0.0;
   }
 }
@@ -886,18 +889,24 @@ static void launch_qt(int grid, const void* x, int64_t n, const float* scale, ui
 }
 
 int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const float* scale, uint8_t* q,
-                           float* amax_acc, hipStream_t st, void* y, int out_dt) {
+                           float* amax, bool reset_amax, hipStream_t st, void* y, int out_dt) {
+  // an overwritten amax is reset on the stream first, then every workgroup
+  // folds its maximum into it; a running one (a scaler's accumulator) is not
+  if (amax && reset_amax) {
+    hipLaunchKernelGGL(k_set_u32, dim3(1), dim3(1), 0, st, (uint32_t*)amax, 0u);
+    if (int e = check_launch("quantize_tensor amax reset")) return e;
+  }
   const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
   const int64_t ch = (int64_t)FP8Q_KU_T * kThreads;
   const int grid = chunk_grid((nvec + ch - 1) / ch, FP8Q_G_T);
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN)
-    launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+    launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax, st, y, out_dt);
   else if (dt == FP8Q_F32)
-    launch_qt<FP8Q_F32, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+    launch_qt<FP8Q_F32, FP8Q_E5M2>(grid, x, n, scale, q, amax, st, y, out_dt);
   else if (fmt == FP8Q_E4M3FN)
-    launch_qt<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+    launch_qt<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, n, scale, q, amax, st, y, out_dt);
   else
-    launch_qt<FP8Q_BF16, FP8Q_E5M2>(grid, x, n, scale, q, amax_acc, st, y, out_dt);
+    launch_qt<FP8Q_BF16, FP8Q_E5M2>(grid, x, n, scale, q, amax, st, y, out_dt);
   return check_launch(y ? "quantize_tensor_dq" : "quantize_tensor");
 }
 

@@ -67,7 +67,10 @@ typedef enum { FP8Q_STAT_MAX = 0, FP8Q_STAT_MEAN = 1, FP8Q_STAT_EMA = 2 } fp8q_w
  * `pos` the next slot, `count` the number of values seen (saturating at
  * window), `scale` the dequantization scale in force, 1.0 until the window
  * fills; `stat` the fp8q_window_stat, `alpha` the EMA coefficient and `ema`
- * the EMA of every amax seen (fp64; 0 unless stat is FP8Q_STAT_EMA). */
+ * the EMA of every amax seen (fp64; 0 unless stat is FP8Q_STAT_EMA).
+ * `amax_acc` is the running amax of the current step: the tensors quantized
+ * with fp8q_quantize_tensor_delayed fold their max|x| into it, and
+ * fp8q_delayed_scaler_update consumes it and sets it back to 0. */
 typedef struct {
   float ring[1024];
   int32_t window;
@@ -79,7 +82,7 @@ typedef struct {
   float scale;
   int32_t stat;
   float alpha;
-  int32_t reserved;
+  float amax_acc;
   double ema;
 } fp8q_scaler;
 
@@ -94,8 +97,10 @@ const char* fp8q_last_error(void);
 
 /* amax = max_i |x_i| over n elements ([A] 4.1; [H] per_tensor).
  * x: n elements of dtype dt, 16-B aligned.  amax: one fp32, overwritten
- * (the call enqueues a 1-thread reset of *amax, then the reduction).
- * A NaN anywhere gives the quiet NaN 0x7FC00000; +-Inf gives +Inf. */
+ * by the reduction's last workgroup (one launch; whatever *amax held
+ * before is ignored).  A NaN anywhere gives the quiet NaN 0x7FC00000;
+ * +-Inf gives +Inf.  Calls in flight at the same time must not share the
+ * amax buffer (different buffers are independent). */
 int fp8q_amax(const void* x, fp8q_dtype dt, int64_t n, float* amax, void* stream);
 
 /* Per-tensor quantization with a scale held in device memory, the form
@@ -104,13 +109,15 @@ int fp8q_amax(const void* x, fp8q_dtype dt, int64_t n, float* amax, void* stream
  * x: n elements of dtype dt, 16-B aligned.  scale: one fp32 dequant scale
  * s, read on the device when the kernel runs (e.g. &state->scale).
  * q: n codes, 16-B aligned.
- * amax_acc: nullable.  When given, the kernel folds max|x| into it as a
- *   running maximum: *amax_acc = max(*amax_acc, amax(x)), with NaN
- *   winning.  It must hold a non-negative value or NaN before the call
- *   (0 after fp8q_delayed_scaler_update, which consumes and resets it).
- *   This fuses the amax of delayed scaling into the same pass over x. */
+ * amax_out: nullable.  When given, *amax_out = max_i |x_i| of this call's
+ *   x, overwritten in the same launch (the last workgroup of the quantizing
+ *   pass writes it; whatever the buffer held before is ignored).  A NaN
+ *   anywhere gives the quiet NaN 0x7FC00000.  This fuses the amax that
+ *   delayed scaling records for the next step into the same pass over x
+ *   ([A] 4.2); hand it to fp8q_delayed_scaler_update.  Calls in flight at
+ *   the same time must not share an amax_out buffer. */
 int fp8q_quantize_tensor(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
-                         uint8_t* q, float* amax_acc, void* stream);
+                         uint8_t* q, float* amax_out, void* stream);
 
 /* fp8q_quantize_tensor that also writes the round trip: y = fl32(dec(q) * s)
  * (fp32, or rounded to nearest-even bf16; NaN -> the quiet NaN), bit for bit
@@ -120,7 +127,24 @@ int fp8q_quantize_tensor(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f,
  * y: n elements of out_dt, 16-B aligned; other arguments and errors as
  * fp8q_quantize_tensor. */
 int fp8q_quantize_tensor_dq(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, const float* scale,
-                            uint8_t* q, float* amax_acc, void* y, fp8q_dtype out_dt, void* stream);
+                            uint8_t* q, float* amax_out, void* y, fp8q_dtype out_dt, void* stream);
+
+/* The per-tensor quantization of one delayed-scaling step ([A] 4.2: the
+ * scale derived from earlier steps quantizes this step's tensor, and this
+ * step's amax is recorded for the next): q = enc(fl32(x / state->scale)),
+ * and max|x| is folded into state->amax_acc as a running maximum (NaN
+ * winning), so several tensors or micro-batches of one step feed one
+ * window entry; fp8q_delayed_scaler_update(state, NULL) then pushes it into
+ * the window and sets it back to 0.  No reset launch is needed: the state
+ * owns the accumulator.  With y non-null the round trip y = fl32(dec(q) *
+ * s) is written in the same pass, as fp8q_quantize_tensor_dq writes it.
+ * x: n elements of dtype dt, 16-B aligned; q: n codes, 16-B aligned; y:
+ * nullable, n elements of out_dt, 16-B aligned; state: initialized by
+ * fp8q_delayed_scaler_init[_stat], 8-B aligned.  Calls that fold into one
+ * state may overlap (the fold is atomic); the update must follow them all
+ * on the stream. */
+int fp8q_quantize_tensor_delayed(const void* x, fp8q_dtype dt, int64_t n, fp8q_format f, fp8q_scaler* state,
+                                 uint8_t* q, void* y, fp8q_dtype out_dt, void* stream);
 
 /* Fine-grained 1x128 quantization of activations ([H] per_block(x, 1,
  * 128); DeepSeek-V3 activation tiling).  For row r and column block kb:
@@ -203,11 +227,13 @@ int fp8q_delayed_scaler_init_stat(fp8q_scaler* state, int32_t window, float max_
                                   float margin, fp8q_window_stat stat, float alpha, void* stream);
 
 /* One delayed-scaling step ([A] 4.2 update): push *amax into the ring
- * (and into the EMA); once `window` values have been seen, scale =
+ * (and into the EMA); amax may be NULL, meaning the state's own amax_acc
+ * (filled by fp8q_quantize_tensor_delayed).  Once `window` values have
+ * been seen, scale =
  * fl32(fl32(max(stat, eps) * margin) / max_val) with stat the state's
  * statistic (max(ring) by default), otherwise the scale stays at its
- * previous value.  *amax is then reset to 0 so it can accumulate the next step
- * (see fp8q_quantize_tensor).  A NaN amax propagates into the scale.
+ * previous value.  *amax is then reset to 0 (the quantizers overwrite it
+ * anyway).  A NaN amax propagates into the scale.
  * Runs as one wavefront; never syncs with the host. */
 int fp8q_delayed_scaler_update(fp8q_scaler* state, float* amax, void* stream);
 

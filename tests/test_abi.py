@@ -137,7 +137,24 @@ def test_scaler_validation(fq):
     assert _rc(fq, "fp8q_delayed_scaler_init", FAKE, 16, -1.0, 1e-12, 1.0, None)[0] == fq.EINVAL
     assert _rc(fq, "fp8q_delayed_scaler_init", FAKE, 16, 448.0, 0.0, 1.0, None)[0] == fq.EINVAL
     assert _rc(fq, "fp8q_delayed_scaler_init", FAKE + 1, 16, 448.0, 1e-12, 1.0, None)[0] == fq.EALIGN
-    assert _rc(fq, "fp8q_delayed_scaler_update", FAKE, None, None)[0] == fq.EINVAL
+    assert _rc(fq, "fp8q_delayed_scaler_update", None, FAKE, None)[0] == fq.EINVAL
+    assert _rc(fq, "fp8q_delayed_scaler_update", None, None, None)[0] == fq.EINVAL
+    # a NULL amax means the state's own accumulator: alignment is still checked
+    assert _rc(fq, "fp8q_delayed_scaler_update", FAKE + 4, None, None)[0] == fq.EALIGN
+    assert _rc(fq, "fp8q_delayed_scaler_update", FAKE, FAKE + 2, None)[0] == fq.EALIGN
+
+
+def test_quantize_tensor_delayed_validation(fq):
+    f = "fp8q_quantize_tensor_delayed"
+    assert _rc(fq, f, FAKE, 1, 1024, 0, None, FAKE, None, 0, None)[0] == fq.EINVAL      # no state
+    assert _rc(fq, f, None, 1, 1024, 0, FAKE, FAKE, None, 0, None)[0] == fq.EINVAL      # no x
+    assert _rc(fq, f, FAKE, 7, 1024, 0, FAKE, FAKE, None, 0, None)[0] == fq.EINVAL      # dtype
+    assert _rc(fq, f, FAKE, 1, 1024, 3, FAKE, FAKE, None, 0, None)[0] == fq.EINVAL      # format
+    assert _rc(fq, f, FAKE, 1, 1024, 0, FAKE, FAKE, FAKE, 9, None)[0] == fq.EINVAL      # round-trip dtype
+    assert _rc(fq, f, FAKE, 1, 0, 0, FAKE, FAKE, None, 0, None)[0] == fq.EINVAL         # n
+    assert _rc(fq, f, FAKE + 2, 1, 1024, 0, FAKE, FAKE, None, 0, None)[0] == fq.EALIGN  # x
+    assert _rc(fq, f, FAKE, 1, 1024, 0, FAKE + 4, FAKE, None, 0, None)[0] == fq.EALIGN  # state
+    assert _rc(fq, f, FAKE, 1, 1024, 0, FAKE, FAKE, FAKE + 8, 0, None)[0] == fq.EALIGN  # y
 
 
 def test_dequantize_validation(fq):

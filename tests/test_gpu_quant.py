@@ -219,25 +219,62 @@ def test_quantize_tensor_round_trip(fq, orc, gpu, dtype, fmt, out):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_quantize_tensor_running_amax(fq, orc, gpu, dtype):
+def test_quantize_tensor_amax_overwrites(fq, orc, gpu, dtype):
+    """The fused amax is written, not accumulated: a caller that hands in
+    whatever buffer it has (a stale larger value, a stale NaN, garbage) gets
+    this call's amax(x); a NaN in x gives the quiet NaN; back-to-back calls
+    on different tensors with no reset in between each get their own."""
     x = W.normal((77_777,), seed=3, std=5.0, dtype=dtype)
     xd = x.to(gpu)
     q = torch.empty(x.numel(), dtype=torch.uint8, device=gpu)
     sd = torch.tensor([0.5], dtype=torch.float32, device=gpu)
-    want = orc.amax(W.to_numpy_input(x))
-    acc = torch.zeros(1, dtype=torch.float32, device=gpu)
-    fq.fp8q_quantize_tensor(xd, x.numel(), E4, sd, q, acc)
-    torch.cuda.synchronize()
-    assert f32bits(acc.cpu().numpy())[0] == f32bits([want])[0]
-    big = torch.tensor([1e9], dtype=torch.float32, device=gpu)
-    fq.fp8q_quantize_tensor(xd, x.numel(), E4, sd, q, big)
-    torch.cuda.synchronize()
-    assert big.item() == 1e9
+    want = f32bits([orc.amax(W.to_numpy_input(x))])[0]
+    for stale in (0.0, 1e9, float("nan"), float("inf"), -3.0):
+        out = torch.tensor([stale], dtype=torch.float32, device=gpu)
+        fq.fp8q_quantize_tensor(xd, x.numel(), E4, sd, q, out)
+        torch.cuda.synchronize()
+        assert f32bits(out.cpu().numpy())[0] == want, stale
     xn = x.clone()
     xn[123] = float("nan")
-    fq.fp8q_quantize_tensor(xn.to(gpu), x.numel(), E4, sd, q, acc)
+    out = torch.zeros(1, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_tensor(xn.to(gpu), x.numel(), E4, sd, q, out)
     torch.cuda.synchronize()
-    assert f32bits(acc.cpu().numpy())[0] == 0x7FC00000
+    assert f32bits(out.cpu().numpy())[0] == 0x7FC00000
+    # the same buffer again, no reset by the caller: the NaN does not stick
+    small = W.normal((4096,), seed=4, std=0.01, dtype=dtype)
+    fq.fp8q_quantize_tensor(small.to(gpu), small.numel(), E4, sd, q, out)
+    torch.cuda.synchronize()
+    assert f32bits(out.cpu().numpy())[0] == f32bits([orc.amax(W.to_numpy_input(small))])[0]
+    # and the round-trip variant
+    y = torch.empty(x.numel(), dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_tensor_dq(xd, x.numel(), E4, sd, q, y, out)
+    torch.cuda.synchronize()
+    assert f32bits(out.cpu().numpy())[0] == want
+
+
+def test_fused_amax_concurrent_calls(fq, orc, gpu):
+    """Per-tensor quantizations and fp8q_amax calls in flight at the same time
+    on eight streams (default priority), each with its own amax output: the
+    one-launch reduction keys its device-side slot by the output, so every
+    output gets its own tensor's amax, over three rounds with no reset."""
+    streams = [torch.cuda.Stream() for _ in range(8)]
+    xs = [W.normal(((1 << 20) + 37 * i,), seed=60 + i, std=float(2 ** i), dtype=torch.bfloat16).to(gpu)
+          for i in range(8)]
+    want = [f32bits([orc.amax(W.to_numpy_input(x.cpu()))])[0] for x in xs]
+    outs = [torch.full((1,), float("nan"), dtype=torch.float32, device=gpu) for _ in range(8)]
+    qs = [torch.empty(x.numel(), dtype=torch.uint8, device=gpu) for x in xs]
+    sd = torch.tensor([0.25], dtype=torch.float32, device=gpu)
+    torch.cuda.synchronize()
+    for rnd in range(3):
+        for i, st in enumerate(streams):
+            with torch.cuda.stream(st):
+                if (i + rnd) % 2:
+                    fq.fp8q_quantize_tensor(xs[i], xs[i].numel(), E4, sd, qs[i], outs[i])
+                else:
+                    fq.fp8q_amax(xs[i], xs[i].numel(), outs[i])
+        torch.cuda.synchronize()
+        for i in range(8):
+            assert f32bits(outs[i].cpu().numpy())[0] == want[i], (rnd, i)
 
 
 # ------------------------------------------------------------------ block quantizers
@@ -559,7 +596,7 @@ def test_scaler_nan_propagates(fq, orc, gpu):
 
 @pytest.mark.parametrize("fmt", [E4, E5])
 def test_delayed_scaling_steps(fq, orc, gpu, fmt):
-    """Fused quantize + running amax + scaler update over 24 steps of a
+    """Fused quantize + amax + scaler update over 24 steps of a
     drifting bf16 sequence (window 4): per-step codes and scales."""
     rows, cols, window = 512, 1024, 4
     sig = W.sigma_schedule(24, seed=2)
@@ -581,4 +618,96 @@ def test_delayed_scaling_steps(fq, orc, gpu, fmt):
         orc.scaler_update(o, float(orc.amax(xn)))
         torch.cuda.synchronize()
         assert_codes_equal(q.cpu().numpy(), want, f"step {t}")
+        assert_scaler_equal(read_scaler(fq, st), o)
+
+
+def test_delayed_scaling_full_config(fq, orc, gpu):
+    """The delayed-scaling workload at its full size: 64 steps over bf16
+    8192x8192 tensors, window 16, the activation copy x_t = bf16(sigma_t
+    N(0,1)) (sigma_t log-uniform in [0.5, 50]) quantized to E4M3FN with its
+    bf16 round trip, and the gradient copy g_t (|g| log-uniform in
+    [1e-6, 1e-2], random sign) to E5M2, each with the scale its scaler
+    derived from the earlier steps and the amax folded into the scaler's
+    accumulator in the same pass (fp8q_quantize_tensor_delayed), then both
+    scalers updated.  Every step: both scaler states (the new amax in the
+    window, the scale) bit-exact against the oracle's sequence; codes
+    bit-exact on 128 sampled rows every step and in full, with x's round
+    trip, on the steps where the scale first moves and a few others."""
+    rows = cols = 8192
+    n = rows * cols
+    steps, window = 64, 16
+    sig = W.sigma_schedule(steps, seed=2)
+    full_steps = {0, 15, 16, 17, 40, steps - 1}
+    sample = np.unique(np.concatenate([np.arange(0, rows, 64) + np.arange(rows // 64) % 64, [rows - 1]]))
+    si = torch.from_numpy(sample).to(gpu)
+    tensors = {
+        "x": (E4, lambda t: W.delayed_step(rows, cols, sig[t], seed=200 + t, device=gpu)),
+        "g": (E5, lambda t: W.gradient(rows, cols, seed=300 + t, device=gpu, dtype=torch.bfloat16)),
+    }
+    state = {}
+    for name, (fmt, _) in tensors.items():
+        st = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=gpu)
+        fq.fp8q_delayed_scaler_init(st, window, MAXF[fmt], EPS, 1.0)
+        state[name] = (st, torch.empty(n, dtype=torch.uint8, device=gpu), orc.scaler_new(window, fmt, EPS, 1.0))
+    y = torch.empty(n, dtype=torch.bfloat16, device=gpu)
+    for t in range(steps):
+        for name, (fmt, make) in tensors.items():
+            st, q, o = state[name]
+            x = make(t)
+            fq.fp8q_quantize_tensor_delayed(x, n, fmt, st, q, y if name == "x" else None)
+            fq.fp8q_delayed_scaler_update(st)
+            xn = W.to_numpy_input(x)
+            s_used = np.float32(o.scale)
+            if t in full_steps:
+                want = orc.quantize_tensor(xn, fmt, s_used)
+                assert_codes_equal(q.cpu().numpy(), want, f"{name} step {t}")
+                if name == "x":
+                    wy = orc.dequantize(want.reshape(1, -1), fmt, np.array([s_used], np.float32), orc.GRAN_TENSOR,
+                                        out_bf16=True).reshape(-1)
+                    assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), wy), f"x round trip step {t}"
+            else:
+                want = orc.quantize_tensor(np.ascontiguousarray(xn.reshape(rows, cols)[sample]), fmt, s_used)
+                assert_codes_equal(q.view(rows, cols)[si].cpu().numpy(), want, f"{name} step {t} (sampled rows)")
+            orc.scaler_update(o, float(orc.amax(xn)))
+            got = read_scaler(fq, st)
+            assert_scaler_equal(got, o)
+            assert got.amax_acc == 0.0, f"{name} accumulator not consumed at step {t}"
+        if t in (0, 16, steps - 1):
+            print(f"step {t}: s_x {state['x'][2].scale:.6g} s_g {state['g'][2].scale:.6g}", flush=True)
+
+
+@pytest.mark.parametrize("fmt", [E4, E5])
+def test_quantize_tensor_delayed_micro_batches(fq, orc, gpu, fmt):
+    """Several micro-batches of one step fold into the one window entry of
+    the step (their joint amax, NaN winning), with no reset between steps;
+    codes and the round trip as the per-tensor quantizer makes them with the
+    state's scale; fp32 and bf16 inputs, ragged lengths."""
+    window = 3
+    st = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=gpu)
+    fq.fp8q_delayed_scaler_init(st, window, MAXF[fmt], EPS, 1.0)
+    o = orc.scaler_new(window, fmt, EPS, 1.0)
+    for t in range(7):
+        amax_step = np.float32(0.0)
+        for mb, (dtype, n) in enumerate([(torch.float32, 70_001), (torch.bfloat16, 4096 * 3 + 5)]):
+            x = W.normal((n,), seed=500 + 10 * t + mb, std=float(3.0 ** (t - 2) * (mb + 1)), dtype=dtype)
+            if t == 4 and mb == 1:
+                x[77] = float("nan")
+            xd = x.to(gpu)
+            q = torch.empty(n, dtype=torch.uint8, device=gpu)
+            y = torch.empty(n, dtype=torch.float32, device=gpu)
+            fq.fp8q_quantize_tensor_delayed(xd, n, fmt, st, q, y)
+            xn = W.to_numpy_input(x)
+            wq = orc.quantize_tensor(xn, fmt, np.float32(o.scale))
+            torch.cuda.synchronize()
+            assert_codes_equal(q.cpu().numpy(), wq, f"step {t} mb {mb}")
+            wy = orc.dequantize(wq.reshape(1, -1), fmt, np.array([o.scale], np.float32), orc.GRAN_TENSOR).reshape(-1)
+            assert np.array_equal(f32bits(y.cpu().numpy()), f32bits(wy))
+            a = orc.amax(xn)
+            amax_step = a if (np.isnan(a) or np.isnan(amax_step)) else max(amax_step, a)
+        got = read_scaler(fq, st)
+        assert f32bits([got.amax_acc])[0] == f32bits([np.float32(np.nan) if np.isnan(amax_step) else amax_step])[0] \
+            or (np.isnan(amax_step) and f32bits([got.amax_acc])[0] == 0x7FC00000)
+        fq.fp8q_delayed_scaler_update(st)
+        orc.scaler_update(o, float(amax_step))
+        torch.cuda.synchronize()
         assert_scaler_equal(read_scaler(fq, st), o)
