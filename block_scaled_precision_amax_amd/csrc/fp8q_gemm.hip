@@ -168,13 +168,26 @@ __device__ __forceinline__ void tile_of(int64_t bid, int64_t nbid, int64_t ntm, 
 }
 
 // LDS layout of a staged R-row x 128-byte code tile: rows are stored
-// unpadded, and the 16-byte chunk c of row r sits in slot c ^ ((r >> 1) & 7)
-// of that row.  Sixteen consecutive rows read at one K offset with 16-byte
-// reads then cover every bank once per 256 bytes (measured on gfx950: the
-// full ~128 B/clk of ds_read_b128, against half of it without the XOR).
+// unpadded, and the 16-byte chunk c of row r sits in slot c ^ f(r) of that
+// row.  A fragment read fetches 16 bytes per lane from sixteen consecutive
+// rows (lane l: row l%16), and the LDS serves a 16-byte read in passes of
+// 16 lanes over 64 four-byte banks, so the 16 lanes of a pass must land on
+// 16 different 16-byte bank groups, ((r & 1) * 8 + slot).  Which lanes share
+// a pass is not documented; the XOR term is chosen so that the reads are
+// conflict-free for every grouping consistent with the counters:
+//   * PAIR (the FP8-MFMA and exact paths: lane group q = l/16 reads chunks
+//     2q and 2q+1): f(r) = (r & 6) | ((r >> 3) & 1).  With the MX layout's
+//     f(r) = (r >> 1) & 7 these reads measured 3.7 bank-conflict cycles per
+//     read (every read served in twice its minimal number of passes, half of
+//     the LDS-active cycles);
+//   * otherwise (MX: chunks q and q+4): f(r) = (r >> 1) & 7 (measured
+//     conflict-free).
 // Every fragment row of a lane has the same r % 16, so the XOR term is a
-// per-lane constant.
-__device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 7); }
+// per-lane constant; f is an XOR, so it maps a row's chunks one to one.
+template <bool PAIR>
+__device__ __forceinline__ int swz_chunk(int r, int c) {
+  return PAIR ? c ^ ((r & 6) | ((r >> 3) & 1)) : c ^ ((r >> 1) & 7);
+}
 
 // Byte offsets (from the operand's base) of the 16-byte chunks a lane copies
 // into LDS for one R-row code tile: the tile is R/8 loads of 1 KB, R/64 per
@@ -183,7 +196,7 @@ __device__ __forceinline__ int swz_chunk(int r, int c) { return c ^ ((r >> 1) & 
 // Rows past the matrix edge read its last row instead (their results are
 // never stored).  The host keeps every operand under 4 GiB so the offsets
 // fit 32 bits.
-template <int R>
+template <int R, bool PAIR>
 __device__ __forceinline__ void dma_offsets(uint32_t* off, int64_t ld, int64_t r0, int64_t rows, int wave,
                                             int lane) {
 #pragma unroll
@@ -191,7 +204,7 @@ __device__ __forceinline__ void dma_offsets(uint32_t* off, int64_t ld, int64_t r
     const int slot = (wave * (R / 64) + u) * 64 + lane, r = slot >> 3, pc = slot & 7;
     int64_t gr = r0 + r;
     gr = gr < rows ? gr : rows - 1;
-    off[u] = (uint32_t)(gr * ld + 16 * swz_chunk(r, pc));
+    off[u] = (uint32_t)(gr * ld + 16 * swz_chunk<PAIR>(r, pc));
   }
 }
 
@@ -433,8 +446,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int64_t sa_r = m0 + (sa_p / (16 * TI)) * 16 * TI + 16 * (sa_p % TI) + (sa_p % (16 * TI)) / TI;
   const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
   uint32_t a_off[BM / 64], b_off[BN / 64];
-  dma_offsets<BM>(a_off, lda, m0, M, wave, lane);
-  dma_offsets<BN>(b_off, ldb, n0, N, wave, lane);
+  dma_offsets<BM, true>(a_off, lda, m0, M, wave, lane);
+  dma_offsets<BN, true>(b_off, ldb, n0, N, wave, lane);
 
   v4f acc[TI][TJ];
 #pragma unroll
@@ -512,7 +525,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     v4f pp[TJ], pn[TJ];
     if constexpr (FAST) {
       // 16x16x128: the lane holds logical chunks 2q, 2q+1 (q = l/16) of its row
-      const int o0 = 16 * swz_chunk(lr, 2 * lq), o1 = 16 * swz_chunk(lr, 2 * lq + 1);
+      const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
       auto frag = [&](const uint8_t* base) {
         const u32x4 x0 = *(const u32x4*)(base + o0);
         const u32x4 x1 = *(const u32x4*)(base + o1);
@@ -548,7 +561,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
       // them going to MFMA kk; A and B use the same assignment, so every
       // product still pairs matching k.  Each lane reads its 32 bytes with
       // two 16-byte LDS reads, as on the FP8 path.
-      const int o0 = 16 * swz_chunk(lr, 2 * lq), o1 = 16 * swz_chunk(lr, 2 * lq + 1);
+      const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
       auto raw32 = [&](const uint8_t* base, u32x2* r) {
         const u32x4 x0 = *(const u32x4*)(base + o0);
         const u32x4 x1 = *(const u32x4*)(base + o1);
@@ -675,7 +688,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     // while computing block kb, whose last row tile publishes block kb+1
     // and decodes its first fragments.
     {
-      const int o0 = 16 * swz_chunk(lr, 2 * lq), o1 = 16 * swz_chunk(lr, 2 * lq + 1);
+      const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
       auto dec32 = [&](const uint8_t* base, auto fmt, typename Mf<H16X>::v8* out) {
         const u32x4 x0 = *(const u32x4*)(base + o0);
         const u32x4 x1 = *(const u32x4*)(base + o1);
@@ -752,8 +765,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
   const int64_t nkb = K / BK;
 
   uint32_t a_off[BM / 64], b_off[BN / 64];
-  dma_offsets<BM>(a_off, lda, m0, M, wave, lane);
-  dma_offsets<BN>(b_off, ldb, n0, N, wave, lane);
+  dma_offsets<BM, false>(a_off, lda, m0, M, wave, lane);
+  dma_offsets<BN, false>(b_off, ldb, n0, N, wave, lane);
   // scales: wavefronts 0-3 copy the 4 bytes (one dword) of A rows
   // 64w + lane, wavefronts 4-7 those of B rows 64(w-4) + lane
   const bool sc_a = wave < 4;
@@ -770,7 +783,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
 
   const int lr = lane & 15, lq = lane >> 4;
   const int a_row0 = wm * TI * 16 + lr, b_row0 = wn * TJ * 16 + lr;
-  const int o0 = 16 * swz_chunk(lr, lq), o1 = 16 * swz_chunk(lr, lq + 4);
+  const int o0 = 16 * swz_chunk<false>(lr, lq), o1 = 16 * swz_chunk<false>(lr, lq + 4);
 
   auto stage_block = [&](int64_t kb, int st) {
     dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
