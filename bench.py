@@ -301,7 +301,27 @@ def run_gpu(steps: int, warmup: int):
     dy, sdy = q1x128(W.gradient(16384, 4096, seed=5, device=dev), fq.E5M2)
     wt, swt = q128(W.weight(4096, 4096, seed=50, device=dev), fq.E4M3FN)
     per["gemm_dgrad"] = gemm_ms(dy, fq.E5M2, sdy, wt, fq.E4M3FN, swt, fq.GRAN_128x128, torch.float32)
-    del dy, sdy, wt, swt
+    # the dgrad's output is the previous layer's gradient: quantized to E5M2
+    # in both layouts that layer needs (1x128 along features for its dgrad,
+    # along tokens for its wgrad) in the epilogue, against the unfused chain
+    # (fp32 C written, then read by the two quantizers)
+    DM, DN, DK = 16384, 4096, 4096
+    gq = torch.empty(DM, DN, dtype=torch.uint8, device=dev)
+    gs_ = torch.empty(DM, DN // 128, dtype=torch.float32, device=dev)
+    gqt = torch.empty(DN, DM, dtype=torch.uint8, device=dev)
+    gst = torch.empty(DN, DM // 128, dtype=torch.float32, device=dev)
+    per["gemm_dgrad_qt"] = per_launch(lambda r: fq.fp8q_gemm_blockscaled_qt(
+        dy, fq.E5M2, DK, sdy, DK // 128, 1, wt, fq.E4M3FN, DK, swt, fq.GRAN_128x128, DK // 128, 1, fq.E5M2, 1e-12,
+        gqt, DM, gst, DM // 128, gq, DN, gs_, DN // 128, DM, DN, DK), 8)
+    Cd = torch.empty(DM, DN, dtype=torch.float32, device=dev)
+
+    def unfused(r):
+        fq.fp8q_gemm_blockscaled(dy, fq.E5M2, DK, sdy, DK // 128, 1, wt, fq.E4M3FN, DK, swt, fq.GRAN_128x128,
+                                 DK // 128, 1, Cd, DN, DM, DN, DK)
+        fq.fp8q_quantize_1x128(Cd, DM, DN, DN, fq.E5M2, 1e-12, gq, DN, gs_, DN // 128)
+        fq.fp8q_quantize_1x128_t(Cd, DM, DN, DN, fq.E5M2, 1e-12, gqt, DM, gst, DM // 128)
+    per["gemm_dgrad_unfused_chain"] = per_launch(unfused, 8)
+    del dy, sdy, wt, swt, gq, gs_, gqt, gst, Cd
     dyt, sdyt = q1x128(W.gradient(4096, 16384, seed=51, device=dev), fq.E5M2)
     # the activations' operand comes from bf16 X [tokens, features] through
     # the transposed 1x128 quantizer (timed here as well)
@@ -604,6 +624,12 @@ def main():
                                                           "E4M3FN x E4M3FN, 1x128 A / 128x128 B scales, bf16 out"),
             "gemm_blockscaled_dgrad_16384x4096x4096": gemm_entry(per["gemm_dgrad"], 16384, 4096, 4096,
                                                                  "E5M2 x E4M3FN, 1x128 A / 128x128 B scales, fp32 out"),
+            "gemm_blockscaled_qt_dgrad_16384x4096x4096": {
+                **gemm_entry(per["gemm_dgrad_qt"], 16384, 4096, 4096,
+                             "E5M2 x E4M3FN, output quantized to E5M2 in the epilogue, 1x128 along N and along M"),
+                "unfused_chain_ms": round(per["gemm_dgrad_unfused_chain"], 4),
+                "note": ("unfused chain: the fp32-out dgrad, then fp8q_quantize_1x128 and fp8q_quantize_1x128_t of "
+                         "its 256 MB output")},
             "gemm_blockscaled_wgrad_4096x4096x16384": gemm_entry(per["gemm_wgrad"], 4096, 4096, 16384,
                                                                  "E5M2 x E4M3FN, 1x128 A and B scales, fp32 out"),
             "quantize_mx_bf16": {"ms": round(per["quantize_mx"], 4), "GB/s": round(q_mx, 1),

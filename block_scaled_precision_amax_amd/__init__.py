@@ -45,6 +45,7 @@ SYMBOLS = (
     "fp8q_gemm_blockscaled_q",
     "fp8q_quantize_tensor_dq",
     "fp8q_quantize_tensor_delayed",
+    "fp8q_gemm_blockscaled_qt",
 )
 
 
@@ -103,6 +104,8 @@ def lib() -> ctypes.CDLL:
             "fp8q_gemm_mx": (i32, [vp, i32, i64, vp, i64, vp, i32, i64, vp, i64, vp, i32, i64, i64, i64, i64, vp]),
             "fp8q_quantize_tensor_dq": (i32, [vp, i32, i64, i32, vp, vp, vp, vp, i32, vp]),
             "fp8q_quantize_tensor_delayed": (i32, [vp, i32, i64, i32, vp, vp, vp, i32, vp]),
+            "fp8q_gemm_blockscaled_qt": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64, i32, f32,
+                                               vp, i64, vp, i64, vp, i64, vp, i64, i64, i64, i64, vp]),
             "fp8q_gemm_blockscaled_q": (i32, [vp, i32, i64, vp, i64, i64, vp, i32, i64, vp, i32, i64, i64, i32, f32,
                                               vp, i64, vp, i64, i64, i64, i64, vp]),
         }
@@ -237,3 +240,10 @@ def fp8q_quantize_tensor_dq(x, n, f, scale, q, y, amax_out=None, stream=None) ->
 def fp8q_quantize_tensor_delayed(x, n, f, state, q, y=None, stream=None) -> None:
     _check(lib().fp8q_quantize_tensor_delayed(_ptr(x), _dt(x), n, f, _ptr(state), _ptr(q), _ptr(y),
                                               _dt(y) if y is not None else F32, _stream(stream, x)))
+
+
+def fp8q_gemm_blockscaled_qt(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb, sB_sn, sB_skb, fc, eps, Cqt, ldcqt,
+                             Cst, ld_cst, Cq, ldcq, Cs, ld_cs, M, N, K, stream=None) -> None:
+    _check(lib().fp8q_gemm_blockscaled_qt(_ptr(A), fa, lda, _ptr(sA), sA_sm, sA_skb, _ptr(B), fb, ldb, _ptr(sB), gb,
+                                          sB_sn, sB_skb, fc, eps, _ptr(Cqt), ldcqt, _ptr(Cst), ld_cst, _ptr(Cq), ldcq,
+                                          _ptr(Cs), ld_cs, M, N, K, _stream(stream, A)))

@@ -302,6 +302,35 @@ int fp8q_gemm_blockscaled_q(const uint8_t* A, fp8q_format fa, int64_t lda, const
                        ld_cs, M, N, K, S(stream));
 }
 
+int fp8q_gemm_blockscaled_qt(const uint8_t* A, fp8q_format fa, int64_t lda, const float* sA, int64_t sA_sm,
+                             int64_t sA_skb, const uint8_t* B, fp8q_format fb, int64_t ldb, const float* sB,
+                             fp8q_gran gb, int64_t sB_sn, int64_t sB_skb, fp8q_format fc, float eps, uint8_t* Cqt,
+                             int64_t ldcqt, float* Cst, int64_t ld_cst, uint8_t* Cq, int64_t ldcq, float* Cs,
+                             int64_t ld_cs, int64_t M, int64_t N, int64_t K, void* stream) {
+  const char* fn = "gemm_blockscaled_qt";
+  if (!A || !sA || !B || !sB || !Cqt || !Cst) return fail(FP8Q_EINVAL, "%s: null pointer", fn);
+  if ((Cq == nullptr) != (Cs == nullptr))
+    return fail(FP8Q_EINVAL, "%s: the row-wise output needs both Cq and Cs (or neither)", fn);
+  if (!valid_fmt(fa) || !valid_fmt(fb) || !valid_fmt(fc)) return fail(FP8Q_EINVAL, "%s: bad format", fn);
+  if (gb != FP8Q_GRAN_128x128 && gb != FP8Q_GRAN_1x128)
+    return fail(FP8Q_EINVAL, "%s: B scales must be 128x128 or 1x128", fn);
+  if (!(eps > 0.0f) || !isfinite(eps)) return fail(FP8Q_EINVAL, "%s: eps must be finite and > 0", fn);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(FP8Q_EINVAL, "%s: M, N, K must be positive", fn);
+  if (K % 128 != 0 || M % 128 != 0)
+    return fail(FP8Q_ESHAPE, "%s: K (%lld) and M (%lld) must be multiples of 128", fn, (long long)K, (long long)M);
+  if (Cq && N % 128 != 0)
+    return fail(FP8Q_ESHAPE, "%s: N (%lld) must be a multiple of 128 for the row-wise output", fn, (long long)N);
+  if (lda < K || ldb < K || ldcqt < M || ld_cst < M / 128 || (Cq && (ldcq < N || ld_cs < N / 128)))
+    return fail(FP8Q_EINVAL, "%s: leading dimension too small", fn);
+  if (sA_sm < 0 || sA_skb < 0 || sB_sn < 0 || sB_skb < 0) return fail(FP8Q_EINVAL, "%s: negative scale stride", fn);
+  if (!aligned(A, 16) || !aligned(B, 16) || lda % 16 != 0 || ldb % 16 != 0 || !aligned(Cqt, 16) || ldcqt % 16 != 0)
+    return fail(FP8Q_EALIGN, "%s: A, B, Cqt and their leading dimensions must be 16-byte aligned", fn);
+  if (!aligned(sA, 4) || !aligned(sB, 4) || !aligned(Cst, 4) || (Cs && !aligned(Cs, 4)))
+    return fail(FP8Q_EALIGN, "%s: misaligned scales", fn);
+  return launch_gemm_qt(A, fa, lda, sA, sA_sm, sA_skb, B, fb, ldb, sB, gb, sB_sn, sB_skb, fc, eps, Cqt, ldcqt, Cst,
+                        ld_cst, Cq, ldcq, Cs, ld_cs, M, N, K, S(stream));
+}
+
 int fp8q_gemm_mx(const uint8_t* A, fp8q_format fa, int64_t lda, const uint8_t* sA, int64_t ld_sa,
                  const uint8_t* B, fp8q_format fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C,
                  fp8q_dtype out_dt, int64_t ldc, int64_t M, int64_t N, int64_t K, void* stream) {

@@ -49,9 +49,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 static constexpr int BK = 128;
 static constexpr int kGemmThreads = 512;  // eight wavefronts, 2 x 4
-// Output kinds beside FP8Q_F32 / FP8Q_BF16: 1x128 FP8 codes of C (E4M3FN or
-// E5M2) with one fp32 scale per 128 columns of a row.
+// Output kinds beside FP8Q_F32 / FP8Q_BF16, each plus the code format
+// (E4M3FN or E5M2): kOutQ, 1x128 FP8 codes of C with one fp32 scale per 128
+// columns of a row; kOutQT, the codes of C^T quantized 1x128 along M (one
+// scale per 128 rows of a column); kOutQB, both.
 static constexpr int kOutQ = 2;
+static constexpr int kOutQT = 4;
+static constexpr int kOutQB = 6;
 
 // Per path: wavefront grid (2 x 4) and MFMA tiles of 16x16 per wavefront.
 // FP8 path: 8 x 4 tiles (128 x 64 per wavefront, 256 x 256 per workgroup);
@@ -323,6 +327,73 @@ __device__ __forceinline__ void epilogue_q(const v4f (&acc)[TI][TJ], uint32_t* l
   }
 }
 
+// 1x128 quantization of C along M in the epilogue: the codes of C^T, one
+// scale per column and 128 consecutive rows (the layout the weight-gradient
+// GEMM takes for a gradient, reduced over tokens).  The exact path's tile
+// is 128 rows high, so a column's 128-row block belongs to the two
+// wavefronts wm = 0, 1 of the same column band (waves w and w ^ 4).  Each
+// takes the maximum |C| of each of its 64 columns over its 64 rows (its
+// four row tiles in registers, the 16 rows of a DPP row by four DPP
+// steps), the two halves meet through LDS, and each element is encoded
+// with its column's s = fl32(max(amax, eps) / MAX) exactly as
+// fp8q_quantize_1x128_t encodes an fp32 input.  The codes are staged in LDS
+// column by column (64 rows per column and wavefront) and leave as 64-byte
+// pieces of the rows of C^T, four lanes per column.  Columns past N are
+// neither stored nor given a scale.
+template <int QF, int TI, int TJ>
+__device__ __forceinline__ void epilogue_qt(const v4f (&acc)[TI][TJ], uint32_t* lds_cmax, uint8_t* stg, int wave,
+                                            int lane, int64_t row0, int64_t col0, int64_t N, float eps,
+                                            uint8_t* __restrict__ Ct, int64_t ldt, float* __restrict__ Cst,
+                                            int64_t ld_st, int64_t mb, bool writes_scale) {
+  static_assert(TI == 4 && TJ == 4, "64 x 64 wavefront tiles");
+  const int lr = lane & 15, lq = lane >> 4;
+  // lane (lr, lq) holds rows 16i + lr and columns 16j + 4lq + e
+  uint32_t cm[TJ][4];
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t m = 0;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) m = max(m, __float_as_uint(acc[i][j][e]) & 0x7FFFFFFFu);
+      cm[j][e] = row16_max(m);
+    }
+  uint32_t* mine = lds_cmax + wave * 64;
+  if (lr == 0) {
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mine[16 * j + 4 * lq + e] = cm[j][e];
+  }
+  __syncthreads();
+  const uint32_t* other = lds_cmax + (wave ^ 4) * 64;
+#pragma unroll
+  for (int j = 0; j < TJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * j + 4 * lq + e;
+      const float amax = __uint_as_float(canon_abs_bits(max(cm[j][e], other[c])));
+      const float s = block_scale<QF>(amax, eps);
+      if (writes_scale && lr == 0 && col0 + c < N) Cst[(col0 + c) * ld_st + mb] = s;
+      const bool fast = scale_ok(s);
+      const float r = 1.0f / s;
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const float x = acc[i][j][e];
+        const uint32_t q = fast ? (cvt2<QF, false>(sat<QF>(div_rn(x, s, r)), 0.0f, 0u) & 0xFFu) : enc1<QF>(x / s);
+        stg[c * 64 + 16 * i + lr] = (uint8_t)q;  // column c, row 16i + lr of the wavefront
+      }
+    }
+  __syncthreads();
+  const int c4 = lane >> 2, k = lane & 3;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int c = 16 * it + c4;
+    const u32x4 v = *(const u32x4*)(stg + c * 64 + 16 * k);
+    if (col0 + c < N) __builtin_nontemporal_store(v, (u32x4*)(Ct + (col0 + c) * ldt + row0 + 16 * k));
+  }
+}
+
 // C leaves through LDS.  In the 16x16 MFMA result (operands swapped, see
 // k_gemm) a lane holds four consecutive columns of one row, so storing
 // straight from registers writes 32-byte (bf16) or 64-byte (fp32) pieces of
@@ -415,7 +486,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
     const uint8_t* __restrict__ A, int64_t lda, const float* __restrict__ sA, int64_t sA_sm,
     int64_t sA_skb, const uint8_t* __restrict__ B, int64_t ldb, const float* __restrict__ sB,
     int64_t sB_sn, int64_t sB_skb, void* __restrict__ C, int64_t ldc, float* __restrict__ Cs,
-    int64_t ld_cs, float qeps, int64_t M, int64_t N, int64_t K, int64_t ntm, int64_t ntn) {
+    int64_t ld_cs, float qeps, uint8_t* __restrict__ Ct, int64_t ldt, float* __restrict__ Cst, int64_t ld_st,
+    int64_t M, int64_t N, int64_t K, int64_t ntm, int64_t ntn) {
   using G = Cfg<FAST>;
   constexpr int BM = G::BM, BN = G::BN, TI = G::TI, TJ = G::TJ, NST = G::NST;
   __shared__ __attribute__((aligned(1024))) uint8_t lds_a[NST][BM * BK];
@@ -425,8 +497,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   constexpr bool SB_COLS = GB == FP8Q_GRAN_1x128;
   __shared__ __attribute__((aligned(16))) float lds_sb[NST][SB_COLS ? BN : 1];
   constexpr int NL = G::NLOAD + (SB_COLS ? 1 : 0);  // loads per wavefront per K block
-  // quantized output: each wavefront's row maxima, read by its neighbour
+  // quantized outputs: each wavefront's row maxima, read by its neighbour,
+  // and its column maxima, read by its partner in the 128-row block
   __shared__ uint32_t lds_rmax[ODT >= kOutQ ? 8 * TI * 16 : 1];
+  __shared__ uint32_t lds_cmax[ODT >= kOutQT ? 8 * TJ * 16 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -724,7 +798,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
                      : 8 * WB <= (int)sizeof(lds_b), "C staging does not fit");
   uint8_t* stg = FAST ? (wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB)
                       : &lds_b[0][0] + wave * WB;
-  if constexpr (ODT >= kOutQ) {
+  if constexpr (ODT >= kOutQT) {
+    static_assert(!FAST, "the quantized outputs are on the exact path");
+    constexpr int QF = ODT & 1;
+    epilogue_qt<QF, TI, TJ>(acc, lds_cmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, N, qeps, Ct, ldt, Cst, ld_st,
+                            m0 / 128, wm == 0);
+    if constexpr (ODT >= kOutQB)
+      epilogue_q<QF, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps, (uint8_t*)C,
+                             ldc, Cs, ld_cs, (wn & 1) == 0);
+  } else if constexpr (ODT >= kOutQ) {
     epilogue_q<ODT - kOutQ, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps,
                                     (uint8_t*)C, ldc, Cs, ld_cs, (wn & 1) == 0);
   } else {
@@ -901,16 +983,24 @@ int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int
   return check_launch("gemm_mx");
 }
 
+// The transposed quantized output (kOutQT, kOutQB) of an exact-path launch.
+struct QtOut {
+  uint8_t* Ct = nullptr;
+  int64_t ldt = 0;
+  float* Cst = nullptr;
+  int64_t ld_st = 0;
+};
+
 template <int FA, int FB, int GB, int ODT, bool FAST>
 static void launch_t(const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
                      const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn, int64_t sB_skb, void* C,
                      int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st, float* Cs = nullptr,
-                     int64_t ld_cs = 0, float qeps = 0.0f) {
+                     int64_t ld_cs = 0, float qeps = 0.0f, QtOut qt = QtOut{}) {
   constexpr int BM = Cfg<FAST>::BM, BN = Cfg<FAST>::BN;
   const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
   hipLaunchKernelGGL((k_gemm<FA, FB, GB, ODT, FAST>), dim3((unsigned)(ntm * ntn)), dim3(kGemmThreads), 0, st, A,
-                     lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, Cs, ld_cs, qeps, M, N, K, ntm,
-                     ntn);
+                     lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, Cs, ld_cs, qeps, qt.Ct, qt.ldt,
+                     qt.Cst, qt.ld_st, M, N, K, ntm, ntn);
 }
 
 template <int FA, int FB, int GB>
@@ -994,6 +1084,63 @@ int launch_gemm_q(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_
   else
     launch_q_f<1, 1>(gb, fc, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldc, Cs, ld_cs, eps, M, N, K, st);
   return check_launch("gemm_blockscaled_q");
+}
+
+template <int FA, int FB, int GB>
+static void launch_qt_g(int fc, bool both, const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm,
+                        int64_t sA_skb, const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn, int64_t sB_skb,
+                        QtOut qt, uint8_t* Cq, int64_t ldcq, float* Cs, int64_t ld_cs, float eps, int64_t M,
+                        int64_t N, int64_t K, hipStream_t st) {
+#define FP8Q_QT_LAUNCH(ODT_)                                                                                 \
+  launch_t<FA, FB, GB, ODT_, false>(A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, Cq, ldcq, M, N, K, st, \
+                                    Cs, ld_cs, eps, qt)
+  if (both) {
+    if (fc == FP8Q_E4M3FN) FP8Q_QT_LAUNCH(kOutQB + FP8Q_E4M3FN);
+    else FP8Q_QT_LAUNCH(kOutQB + FP8Q_E5M2);
+  } else {
+    if (fc == FP8Q_E4M3FN) FP8Q_QT_LAUNCH(kOutQT + FP8Q_E4M3FN);
+    else FP8Q_QT_LAUNCH(kOutQT + FP8Q_E5M2);
+  }
+#undef FP8Q_QT_LAUNCH
+}
+
+template <int FA, int FB>
+static void launch_qt_f(int gb, int fc, bool both, const uint8_t* A, int64_t lda, const float* sA, int64_t sA_sm,
+                        int64_t sA_skb, const uint8_t* B, int64_t ldb, const float* sB, int64_t sB_sn,
+                        int64_t sB_skb, QtOut qt, uint8_t* Cq, int64_t ldcq, float* Cs, int64_t ld_cs, float eps,
+                        int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (gb == FP8Q_GRAN_128x128)
+    launch_qt_g<FA, FB, FP8Q_GRAN_128x128>(fc, both, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, qt, Cq,
+                                           ldcq, Cs, ld_cs, eps, M, N, K, st);
+  else
+    launch_qt_g<FA, FB, FP8Q_GRAN_1x128>(fc, both, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, qt, Cq,
+                                         ldcq, Cs, ld_cs, eps, M, N, K, st);
+}
+
+int launch_gemm_qt(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
+                   const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb, int64_t sB_sn, int64_t sB_skb,
+                   int fc, float eps, uint8_t* Ct, int64_t ldt, float* Cst, int64_t ld_st, uint8_t* Cq, int64_t ldcq,
+                   float* Cs, int64_t ld_cs, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  const int64_t tiles = ((M + 127) / 128) * ((N + 255) / 256);
+  if (tiles > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "gemm_qt: more than 2^31-1 output tiles");
+  if ((M - 1) * lda + K > 0xFFFFFFFFll || (N - 1) * ldb + K > 0xFFFFFFFFll ||
+      (gb == FP8Q_GRAN_1x128 && (N - 1) * sB_sn > 0x3FFFFFFFll))
+    return fail(FP8Q_ESHAPE, "gemm_qt: an operand spans 4 GiB or more");
+  const QtOut qt{Ct, ldt, Cst, ld_st};
+  const bool both = Cq != nullptr;
+  if (fa == FP8Q_E4M3FN && fb == FP8Q_E4M3FN)
+    launch_qt_f<0, 0>(gb, fc, both, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, qt, Cq, ldcq, Cs, ld_cs,
+                      eps, M, N, K, st);
+  else if (fa == FP8Q_E5M2 && fb == FP8Q_E4M3FN)
+    launch_qt_f<1, 0>(gb, fc, both, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, qt, Cq, ldcq, Cs, ld_cs,
+                      eps, M, N, K, st);
+  else if (fa == FP8Q_E4M3FN && fb == FP8Q_E5M2)
+    launch_qt_f<0, 1>(gb, fc, both, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, qt, Cq, ldcq, Cs, ld_cs,
+                      eps, M, N, K, st);
+  else
+    launch_qt_f<1, 1>(gb, fc, both, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, qt, Cq, ldcq, Cs, ld_cs,
+                      eps, M, N, K, st);
+  return check_launch("gemm_blockscaled_qt");
 }
 
 int launch_gemm(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm,

@@ -165,6 +165,10 @@ int launch_gemm_q(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_
                   const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb, int64_t sB_sn, int64_t sB_skb,
                   int fc, float eps, uint8_t* Cq, int64_t ldc, float* Cs, int64_t ld_cs, int64_t M, int64_t N,
                   int64_t K, hipStream_t st);
+int launch_gemm_qt(const uint8_t* A, int fa, int64_t lda, const float* sA, int64_t sA_sm, int64_t sA_skb,
+                   const uint8_t* B, int fb, int64_t ldb, const float* sB, int gb, int64_t sB_sn, int64_t sB_skb,
+                   int fc, float eps, uint8_t* Ct, int64_t ldt, float* Cst, int64_t ld_st, uint8_t* Cq, int64_t ldcq,
+                   float* Cs, int64_t ld_cs, int64_t M, int64_t N, int64_t K, hipStream_t st);
 int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
                    int fb, int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C, int out_dt, int64_t ldc,
                    int64_t M, int64_t N, int64_t K, hipStream_t st);

@@ -304,6 +304,31 @@ int fp8q_gemm_blockscaled_q(const uint8_t* A, fp8q_format fa, int64_t lda, const
                             int64_t ldcq, float* Cs, int64_t ld_cs, int64_t M, int64_t N, int64_t K,
                             void* stream);
 
+/* fp8q_gemm_blockscaled with the output quantized along M in the epilogue,
+ * for a gradient produced by this GEMM (a dgrad whose output is the
+ * previous layer's output gradient): the previous layer's weight-gradient
+ * GEMM reduces over tokens (M), so it takes C^T as codes with one scale per
+ * 128 tokens ([H] fine-grained 1x128 scaling along the reduced dimension;
+ * [A] 6.3 gradients in E5M2; [A] 5.1 casts to and from a wide type between
+ * FP8 operations eat the gain).  The fp32 C of fp8q_gemm_blockscaled is
+ * never written; instead, per column n and 128 consecutive rows,
+ *   Cst[n*ld_cst + m/128] = fl32(max(amax(C[128(m/128) : +128, n]), eps) / MAX_fc),
+ *   Cqt[n*ldcqt + m]     = enc_fc(fl32(C[m,n] / s)),
+ * bit for bit what fp8q_quantize_1x128_t makes of that fp32 C.  With Cq and
+ * Cs non-null the same epilogue also writes the row-wise output of
+ * fp8q_gemm_blockscaled_q (what the previous layer's dgrad takes), from the
+ * same accumulators.
+ * Arguments as fp8q_gemm_blockscaled (exact path) plus: fc the output
+ * format, eps > 0; Cqt [N, M] codes, ldcqt >= M, Cqt and ldcqt 16-B
+ * aligned; Cst [N, M/128] fp32, ld_cst >= M/128; Cq, Cs nullable together
+ * (ldcq >= N, ld_cs >= N/128).  M % 128 == 0 and K % 128 == 0, and
+ * N % 128 == 0 when Cq is given (else FP8Q_ESHAPE); otherwise N >= 1. */
+int fp8q_gemm_blockscaled_qt(const uint8_t* A, fp8q_format fa, int64_t lda, const float* sA, int64_t sA_sm,
+                             int64_t sA_skb, const uint8_t* B, fp8q_format fb, int64_t ldb, const float* sB,
+                             fp8q_gran gb, int64_t sB_sn, int64_t sB_skb, fp8q_format fc, float eps, uint8_t* Cqt,
+                             int64_t ldcqt, float* Cst, int64_t ld_cst, uint8_t* Cq, int64_t ldcq, float* Cs,
+                             int64_t ld_cs, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* MX GEMM ([H] FP8 training, hardware note: 32 elements share one scale
  * factor in hardware): C[m,n] = sum over 32-element K blocks kb of
  *   2^(sA[m,kb] - 127) * 2^(sB[n,kb] - 127) * sum_{k in kb} dec(A[m,k]) dec(B[n,k]),

@@ -258,6 +258,18 @@ def gemm_blockscaled_q(A: np.ndarray, fa: int, sA: np.ndarray, B: np.ndarray, fb
     return q, s, C32
 
 
+def gemm_blockscaled_qt(A: np.ndarray, fa: int, sA: np.ndarray, B: np.ndarray, fb: int, sB: np.ndarray, gb: int,
+                        fc: int, eps: float = EPS):
+    """The GEMM's output quantized along M for the weight gradient: C = fl32 of
+    the exact block-scaled product (gemm_blockscaled), then quantize_blocks(C,
+    128, 1, fc, eps) -- one scale per 128 rows of a column -- returned as the
+    codes of C^T [N, M] and their scales [N, M/128], with C fp32."""
+    C, _ = gemm_blockscaled(A, fa, sA, B, fb, sB, gb)
+    C32 = C.astype(np.float32)  # round to nearest even
+    q, s = quantize_blocks(C32, 128, 1, fc, eps)
+    return np.ascontiguousarray(q.T), np.ascontiguousarray(s.T), C32
+
+
 def quantize_mx(x: np.ndarray, fmt: int):
     """32-element blocks along rows with power-of-two E8M0 scales (OCP MX v1.0, 6.3).
     Returns (codes [rows, cols], scale bytes [rows, cols/32])."""

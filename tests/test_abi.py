@@ -157,6 +157,35 @@ def test_quantize_tensor_delayed_validation(fq):
     assert _rc(fq, f, FAKE, 1, 1024, 0, FAKE, FAKE, FAKE + 8, 0, None)[0] == fq.EALIGN  # y
 
 
+def test_gemm_qt_validation(fq):
+    ok = dict(A=FAKE, fa=1, lda=256, sA=FAKE, sA_sm=2, sA_skb=1, B=FAKE, fb=0, ldb=256, sB=FAKE, gb=2, sB_sn=2,
+              sB_skb=1, fc=1, eps=1e-12, Ct=FAKE, ldt=256, Cst=FAKE, ld_st=2, Cq=None, ldcq=128, Cs=None, ld_cs=1,
+              M=256, N=128, K=256)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return _rc(fq, "fp8q_gemm_blockscaled_qt", a["A"], a["fa"], a["lda"], a["sA"], a["sA_sm"], a["sA_skb"],
+                   a["B"], a["fb"], a["ldb"], a["sB"], a["gb"], a["sB_sn"], a["sB_skb"], a["fc"],
+                   ctypes.c_float(a["eps"]), a["Ct"], a["ldt"], a["Cst"], a["ld_st"], a["Cq"], a["ldcq"], a["Cs"],
+                   a["ld_cs"], a["M"], a["N"], a["K"], None)
+
+    assert call(Ct=None)[0] == fq.EINVAL
+    assert call(Cst=None)[0] == fq.EINVAL
+    assert call(Cq=FAKE)[0] == fq.EINVAL           # Cq without Cs
+    assert call(fc=2)[0] == fq.EINVAL
+    assert call(eps=0.0)[0] == fq.EINVAL
+    rc, msg = call(M=200, ldt=256)
+    assert rc == fq.ESHAPE and "multiples of 128" in msg
+    assert call(K=200, lda=256, ldb=256)[0] == fq.ESHAPE
+    assert call(N=100, Cq=FAKE, Cs=FAKE)[0] == fq.ESHAPE   # the row-wise output needs N % 128 == 0
+    assert call(ldt=128)[0] == fq.EINVAL
+    assert call(ld_st=1)[0] == fq.EINVAL
+    assert call(Cq=FAKE, Cs=FAKE, ldcq=64)[0] == fq.EINVAL
+    assert call(Ct=FAKE + 8)[0] == fq.EALIGN
+    assert call(ldt=264)[0] == fq.EALIGN
+    assert call(Cst=FAKE + 2)[0] == fq.EALIGN
+
+
 def test_dequantize_validation(fq):
     f = "fp8q_dequantize"
     assert _rc(fq, f, FAKE, 0, 4, 256, 256, FAKE, 5, 2, FAKE, 0, 256, None)[0] == fq.EINVAL  # gran

@@ -437,3 +437,136 @@ def test_gemm_q_layer_sampled(fq, orc, gpu):
     y = (dec.reshape(len(rows), N // 128, 128) * s[:, :, None]).reshape(len(rows), N)
     bound = 2.0 ** -4 * np.abs(Cref) + 2.0 ** -10 * np.repeat(s, 128, axis=1) + 2 * TOL * D
     assert np.all(np.abs(y - Cref) <= bound)
+
+
+# ------------------------------------------------------------------ quantized along M (transposed output)
+def run_gemm_qt(fq, A, fa, sA, B, fb, sB, gb, fc, both=False, dev="cuda"):
+    """fp8q_gemm_blockscaled_qt with padded outputs (the padding must keep its
+    bytes); returns (codes of C^T [N, M], scales [N, M/128], row-wise codes,
+    row-wise scales) with the last two None unless `both`."""
+    M, K = A.shape
+    N = B.shape[0]
+    ldt, ld_st = M + 32, M // 128 + 2
+    qt = torch.full((N, ldt), 0xAA, dtype=torch.uint8, device=dev)
+    st = torch.full((N, ld_st), -7.0, dtype=torch.float32, device=dev)
+    q = s = None
+    if both:
+        q = torch.full((M, N + 16), 0xAA, dtype=torch.uint8, device=dev)
+        s = torch.full((M, N // 128 + 1), -7.0, dtype=torch.float32, device=dev)
+    fq.fp8q_gemm_blockscaled_qt(A.to(dev), fa, K, sA.to(dev), sA.shape[1], 1, B.to(dev), fb, K, sB.to(dev), gb,
+                                sB.shape[1], 1, fc, 1e-12, qt, ldt, st, ld_st, q, N + 16, s, N // 128 + 1, M, N, K)
+    torch.cuda.synchronize()
+    qt, st = qt.cpu(), st.cpu()
+    assert torch.all(qt[:, M:] == 0xAA) and torch.all(st[:, M // 128:] == -7.0), "wrote past a row of C^T"
+    out = [qt[:, :M].numpy(), st[:, :M // 128].numpy(), None, None]
+    if both:
+        q, s = q.cpu(), s.cpu()
+        assert torch.all(q[:, N:] == 0xAA) and torch.all(s[:, N // 128:] == -7.0), "wrote past a row of C"
+        out[2], out[3] = q[:, :N].numpy(), s[:, :N // 128].numpy()
+    return out
+
+
+@pytest.mark.parametrize("fa,fb,gb,fc", [(E5, E4, G128, E5), (E4, E4, G128, E4), (E5, E4, G1, E5),
+                                         (E4, E5, G1, E4)])
+@pytest.mark.parametrize("M,N,K", [(128, 128, 128), (256, 384, 512), (384, 200, 256), (128, 64, 1024),
+                                   (256, 1, 128), (512, 640, 384)])
+def test_gemm_qt_exact_inputs_match_oracle(fq, orc, gpu, fa, fb, gb, fc, M, N, K):
+    """Integer codes and power-of-two scales (exact sums): the codes of C^T
+    and their scales along M bit-identical to the oracle's quantize_blocks(
+    fl32(C_exact), 128, 1) -- one scale per 128 rows of a column -- over
+    several 128-row blocks and tiles, a ragged N (200, 1, 64: the transposed
+    output alone), and, where N % 128 == 0, the row-wise output written by
+    the same epilogue bit-identical to the oracle's quantize_1x128."""
+    A = int_codes(orc, (M, K), fa, M + K + 3)
+    B = int_codes(orc, (N, K), fb, N + K + 4)
+    sA = pow2_scales((M, K // 128), 5)
+    sB = pow2_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 6)
+    both = N % 128 == 0
+    qt, st, q, s = run_gemm_qt(fq, A, fa, sA, B, fb, sB, gb, fc, both=both)
+    wqt, wst, _ = orc.gemm_blockscaled_qt(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb, fc)
+    assert np.array_equal(st.view(np.uint32), wst.view(np.uint32))
+    assert np.array_equal(qt, wqt)
+    if both:
+        wq, ws, _ = orc.gemm_blockscaled_q(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb, fc)
+        assert np.array_equal(s.view(np.uint32), ws.view(np.uint32))
+        assert np.array_equal(q, wq)
+
+
+@pytest.mark.parametrize("fa,fb,gb,fc,special", [(E5, E4, G128, E5, False), (E4, E4, G1, E4, False),
+                                                 (E5, E4, G128, E5, True)])
+def test_gemm_qt_equals_gemm_then_transposed_quantize(fq, orc, gpu, fa, fb, gb, fc, special):
+    """Random codes over the whole code space and random scales: the codes
+    of C^T and their scales are bit for bit fp8q_quantize_1x128_t of
+    fp8q_gemm_blockscaled's fp32 C, and the row-wise output bit for bit
+    fp8q_quantize_1x128 of it.  The special case puts a NaN code in one A
+    row (every column's first 128-row block becomes NaN: scale NaN, codes
+    0x7F) and one B row (a whole column of C^T), and zeros one A row."""
+    M, N, K = 384, 640, 768
+    A = W.fp8_codes((M, K), fa, seed=81)
+    B = W.fp8_codes((N, K), fb, seed=82)
+    if special:
+        A[3, 5] = 0x7F
+        B[200, 77] = 0xFF
+        A[300, :] = 0
+    sA = rand_scales((M, K // 128), 83)
+    sB = rand_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 84)
+    qt, st, q, s = run_gemm_qt(fq, A, fa, sA, B, fb, sB, gb, fc, both=True)
+    C = run_gemm(fq, A, fa, sA, B, fb, sB, gb).to(gpu)
+    qt2 = torch.empty(N, M, dtype=torch.uint8, device=gpu)
+    st2 = torch.empty(N, M // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_1x128_t(C, M, N, N, fc, 1e-12, qt2, M, st2, M // 128)
+    q2 = torch.empty(M, N, dtype=torch.uint8, device=gpu)
+    s2 = torch.empty(M, N // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_1x128(C, M, N, N, fc, 1e-12, q2, N, s2, N // 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(st.view(np.uint32), st2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(qt, qt2.cpu().numpy())
+    assert np.array_equal(s.view(np.uint32), s2.cpu().numpy().view(np.uint32))
+    assert np.array_equal(q, q2.cpu().numpy())
+    if special:
+        assert np.all(np.isnan(st[:, 0])) and np.all(qt[:, :128] == 0x7F)
+        assert np.all(np.isnan(st[200])) and np.all(qt[200] == 0x7F)
+        assert np.all(np.isfinite(st[np.arange(N) != 200, 1:]))
+
+
+def test_gemm_qt_dgrad_full_size(fq, orc, gpu):
+    """The backward-shaped dgrad 16384 x 4096 x 4096 (E5M2 gradients 1x128 x
+    E4M3FN transposed weight 128x128) with its output -- the previous
+    layer's gradient -- quantized to E5M2 in both layouts by the epilogue:
+    bit for bit the unfused GEMM's fp32 C quantized by fp8q_quantize_1x128_t
+    and fp8q_quantize_1x128, over the whole output; the fp32 C itself is
+    checked against the oracle on one row per 128-row band."""
+    M, N, K = 16384, 4096, 4096
+    g = W.gradient(M, K, seed=5, device=gpu)
+    w = W.weight(N, K, seed=50, device=gpu)
+    qa = torch.empty(M, K, dtype=torch.uint8, device=gpu)
+    sa = torch.empty(M, K // 128, dtype=torch.float32, device=gpu)
+    qb = torch.empty(N, K, dtype=torch.uint8, device=gpu)
+    sb = torch.empty(N // 128, K // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_quantize_1x128(g, M, K, K, E5, 1e-12, qa, K, sa, K // 128)
+    fq.fp8q_quantize_128x128(w, N, K, K, E4, 1e-12, qb, K, sb, K // 128)
+    del g, w
+    qt = torch.empty(N, M, dtype=torch.uint8, device=gpu)
+    st = torch.empty(N, M // 128, dtype=torch.float32, device=gpu)
+    q = torch.empty(M, N, dtype=torch.uint8, device=gpu)
+    s = torch.empty(M, N // 128, dtype=torch.float32, device=gpu)
+    fq.fp8q_gemm_blockscaled_qt(qa, E5, K, sa, K // 128, 1, qb, E4, K, sb, G128, K // 128, 1, E5, 1e-12, qt, M, st,
+                                M // 128, q, N, s, N // 128, M, N, K)
+    C = torch.empty(M, N, dtype=torch.float32, device=gpu)
+    fq.fp8q_gemm_blockscaled(qa, E5, K, sa, K // 128, 1, qb, E4, K, sb, G128, K // 128, 1, C, N, M, N, K)
+    qt2 = torch.empty_like(qt)
+    st2 = torch.empty_like(st)
+    fq.fp8q_quantize_1x128_t(C, M, N, N, E5, 1e-12, qt2, M, st2, M // 128)
+    q2 = torch.empty_like(q)
+    s2 = torch.empty_like(s)
+    fq.fp8q_quantize_1x128(C, M, N, N, E5, 1e-12, q2, N, s2, N // 128)
+    torch.cuda.synchronize()
+    assert torch.equal(st.view(torch.int32), st2.view(torch.int32))
+    assert torch.equal(qt, qt2)
+    assert torch.equal(s.view(torch.int32), s2.view(torch.int32))
+    assert torch.equal(q, q2)
+    rows = band_rows(M)
+    ri = torch.from_numpy(rows).to(gpu)
+    Cref, D = orc.gemm_blockscaled(qa[ri].cpu().numpy(), E5, sa[ri].cpu().numpy(), qb.cpu().numpy(), E4,
+                                   sb.cpu().numpy(), G128)
+    check(C[ri].cpu(), Cref, D, "dgrad")
