@@ -83,10 +83,13 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 #define FP8Q_KU_T 2
 #endif
 #ifndef FP8Q_G_T
-#define FP8Q_G_T 16
+#define FP8Q_G_T 8
+#endif
+#ifndef FP8Q_G_MX
+#define FP8Q_G_MX 16
 #endif
 #ifndef FP8Q_G_1
-#define FP8Q_G_1 12
+#define FP8Q_G_1 8
 #endif
 #ifndef FP8Q_KU_D
 #define FP8Q_KU_D 4
@@ -446,10 +449,8 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restri
   const int f = tid >> 2, k = tid & 3;
   const int fc = f ^ (16 * k);
   const int64_t col = c0 + f;
-  u32x4 v[NVT], vn[NVT];
-  load(rb_begin, v);
-  for (int64_t rb = rb_begin; rb < rb_end; ++rb) {
-    if (rb + 1 < rb_end) load(rb + 1, vn);
+  // One row block: stage the tile, reduce each column's amax, encode, store.
+  auto block = [&](int64_t rb, const u32x4* v) {
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
       const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
@@ -490,9 +491,22 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restri
     uint8_t* qrow = q + col * ldq + rb * 128 + 16 * k;
     __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)qrow);
     __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, (u32x4*)(qrow + 64));
+  };
+  // The next block's loads are issued unconditionally before the current
+  // block is used (the last block is peeled off), so the wait before the
+  // tile is staged leaves them in flight: issued under a condition, the
+  // compiler cannot count them and waits for every load, the prefetch
+  // included, which serializes the loads with the block's work.
+  u32x4 v[NVT], vn[NVT];
+  load(rb_begin, v);
+  int64_t rb = rb_begin;
+  for (; rb + 1 < rb_end; ++rb) {
+    load(rb + 1, vn);
+    block(rb, v);
 #pragma unroll
     for (int i = 0; i < NVT; ++i) v[i] = vn[i];
   }
+  block(rb, v);
 }
 
 // ---------------------------------------------------------------- 128x128
@@ -1037,7 +1051,7 @@ int launch_quantize_mx(const void* x, int dt, int64_t rows, int64_t cols, int64_
   // contiguous chunks of whole thread-steps; a chunk is a multiple of 32
   // elements' lanes, so no block is split between workgroups
   const int64_t steps = (nvec + kThreads - 1) / kThreads;
-  const int grid = chunk_grid(steps, FP8Q_G_T);
+  const int grid = chunk_grid(steps, FP8Q_G_MX);
   const int64_t per_wg = ((steps + grid - 1) / grid) * kThreads;
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_qmx<FP8Q_F32, FP8Q_E4M3FN>(grid, x, vpr, nvec, ldx, q, ldq, scales, ld_s, per_wg, st);
   else if (dt == FP8Q_F32) launch_qmx<FP8Q_F32, FP8Q_E5M2>(grid, x, vpr, nvec, ldx, q, ldq, scales, ld_s, per_wg, st);

@@ -416,8 +416,10 @@ def oracle_t(orc, x_np, fmt):
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("rows,cols,ldx,pad_q", [(128, 64, 64, 0), (256, 192, 200, 32), (384, 128, 136, 16),
-                                                 (128, 1024, 1024, 0)])
+                                                 (128, 1024, 1024, 0), (384, 512, 520, 16), (640, 768, 768, 0)])
 def test_quantize_1x128_t(fq, orc, gpu, dt, fmt, rows, cols, ldx, pad_q):
+    """Padded rows, one and several 64-column slabs, several 128-row blocks
+    per workgroup."""
     rng = np.random.default_rng(rows + cols + fmt)
     x = (rng.standard_normal((rows, ldx)) * np.exp(rng.standard_normal((1, ldx)) * 3)).astype(np.float32)
     xd = torch.from_numpy(x).to(dt).to(gpu)
@@ -430,13 +432,14 @@ def test_quantize_1x128_t(fq, orc, gpu, dt, fmt, rows, cols, ldx, pad_q):
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("fmt", [E4, E5])
-def test_quantize_1x128_t_special_values(fq, orc, gpu, dt, fmt):
+@pytest.mark.parametrize("ncols", [64, 256])
+def test_quantize_1x128_t_special_values(fq, orc, gpu, dt, fmt, ncols):
     """Every special block (zeros, NaN, Inf, denormals, below eps, huge,
-    rounding midpoints) as 128-row column segments."""
-    x = np.ascontiguousarray(special_blocks_fp32(np.random.default_rng(11), 64).T)  # 1024 x 64
+    rounding midpoints) as 128-row column segments, one and four slabs."""
+    x = np.ascontiguousarray(special_blocks_fp32(np.random.default_rng(11), ncols).T)  # 1024 x ncols
     xd = torch.from_numpy(x).to(dt).to(gpu)
     xv = W.to_numpy_input(xd.cpu())
-    q, s = run_block_t(fq, xd, 1024, 64, 64, fmt)
+    q, s = run_block_t(fq, xd, 1024, ncols, ncols, fmt)
     wq, ws = oracle_t(orc, xv, fmt)
     assert_codes_equal(q, wq)
     assert np.array_equal(f32bits(s), f32bits(ws))
