@@ -398,7 +398,7 @@ def stream_ceiling(dev, per_launch):
     L = ctypes.CDLL(B.STREAM_LIB)
     L.fp8q_stream_ref.restype = ctypes.c_int
     L.fp8q_stream_ref.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
-                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+                                  ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     src = torch.ones(STREAM_READ_BYTES // 4 + 1024, dtype=torch.float32, device=dev)
     dst = torch.empty(2 * STREAM_READ_BYTES // 4 + 1024, dtype=torch.float32, device=dev)
@@ -406,18 +406,20 @@ def stream_ceiling(dev, per_launch):
     for kind, (rd, wr) in STREAM_KINDS.items():
         items = STREAM_READ_BYTES // rd
         best = None
-        for u in (2, 4, 8):
-            for g in (4, 8, 16):
-                def launch(r, u=u, g=g):
-                    rc = L.fp8q_stream_ref(src.data_ptr(), dst.data_ptr(), items, rd, wr, u, g, cus,
-                                           torch.cuda.current_stream().cuda_stream)
-                    if rc != 0:
-                        raise RuntimeError(f"fp8q_stream_ref failed: {rc}")
-                ms = per_launch(launch, 8)
-                gbs = items * (rd + wr) / (ms * 1e-3) / 1e9
-                if best is None or gbs > best["GB/s"]:
-                    best = {"GB/s": round(gbs, 1), "ms": round(ms, 4), "vectors_per_lane": u, "wg_per_cu": g,
-                            "read_bytes": items * rd, "write_bytes": items * wr}
+        # 256-thread workgroups (the quantizers' size) and 1024-thread ones
+        sweep = [(256, u, g) for u in (2, 4, 8) for g in (4, 8, 16)] + \
+                [(1024, u, g) for u in (1, 2) for g in (1, 2, 4)]
+        for th, u, g in sweep:
+            def launch(r, u=u, g=g, th=th):
+                rc = L.fp8q_stream_ref(src.data_ptr(), dst.data_ptr(), items, rd, wr, u, g, cus, th,
+                                       torch.cuda.current_stream().cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"fp8q_stream_ref failed: {rc}")
+            ms = per_launch(launch, 8)
+            gbs = items * (rd + wr) / (ms * 1e-3) / 1e9
+            if best is None or gbs > best["GB/s"]:
+                best = {"GB/s": round(gbs, 1), "ms": round(ms, 4), "threads": th, "vectors_per_lane": u,
+                        "wg_per_cu": g, "read_bytes": items * rd, "write_bytes": items * wr}
         best["frac_hbm"] = round(best["GB/s"] / HBM_PEAK_GBPS, 4)
         out[kind] = best
     del src, dst
@@ -643,8 +645,8 @@ def main():
                         "operands": "MX E4M3FN x MX E4M3FN, scaled FP8 MFMA, bf16 out, the layer's shape"},
             "stream_ceiling": {**per["stream"],
                                "note": ("hand-written 16-B-per-lane streams (libfp8q_stream.so), best of a sweep of "
-                                        "chunk depth and grid size, about 1 GiB read each: the attainable HBM rate "
-                                        "for each read:write proportion")},
+                                        "chunk depth, grid size and workgroup size (256 or 1024 threads), about "
+                                        "1 GiB read each: the attainable HBM rate for each read:write proportion")},
             "copy_reference_fp32": {"ms": round(per["copy_reference"], 4), "GB/s": round(cp, 1),
                                     "frac_hbm": round(cp / HBM_PEAK_GBPS, 4),
                                     "note": "torch elementwise pass, 1 GiB in + 1 GiB out: attainable streaming rate"},

@@ -35,15 +35,16 @@ __device__ __forceinline__ uint32_t pk_fold(uint32_t acc) {
   return max(acc & 0xFFFFu, acc >> 16) << 16;
 }
 
-// Workgroup-wide maximum of one value per thread (kThreads threads).
+// Workgroup-wide maximum of one value per thread (TH threads).
+template <int TH = kThreads>
 __device__ __forceinline__ uint32_t block_max(uint32_t v) {
-  __shared__ uint32_t part[kThreads / 64];
+  __shared__ uint32_t part[TH / 64];
   v = wave_max(v);
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
   __syncthreads();
   uint32_t m = part[0];
 #pragma unroll
-  for (int i = 1; i < kThreads / 64; ++i) m = max(m, part[i]);
+  for (int i = 1; i < TH / 64; ++i) m = max(m, part[i]);
   __syncthreads();
   return m;
 }
@@ -84,6 +85,9 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 #endif
 #ifndef FP8Q_G_T
 #define FP8Q_G_T 8
+#endif
+#ifndef FP8Q_TH_T
+#define FP8Q_TH_T 256  // threads per workgroup of the per-tensor quantizer
 #endif
 #ifndef FP8Q_G_MX
 #define FP8Q_G_MX 16
@@ -201,18 +205,18 @@ __device__ __forceinline__ void store_dq4(uint32_t w, float s, void* __restrict_
 template <int DT, int FMT, bool FAST, int ODT>
 __device__ __forceinline__ uint32_t tensor_stream(const u32x4* __restrict__ xv, int64_t nvec, float s,
                                                   float r, uint8_t* __restrict__ q, void* __restrict__ y) {
-  constexpr int kU = FP8Q_KU_T;
-  constexpr int64_t kChunk = (int64_t)kU * kThreads;
+  constexpr int kU = FP8Q_KU_T, TH = FP8Q_TH_T;
+  constexpr int64_t kChunk = (int64_t)kU * TH;
   uint32_t m = 0;
   for (int64_t c = blockIdx.x; c * kChunk < nvec; c += gridDim.x) {
     const int64_t base = c * kChunk + threadIdx.x;
     u32x4 v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (base + u * kThreads < nvec) v[u] = __builtin_nontemporal_load(xv + base + u * kThreads);
+      if (base + u * TH < nvec) v[u] = __builtin_nontemporal_load(xv + base + u * TH);
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int64_t i = base + u * kThreads;
+      const int64_t i = base + u * TH;
       if (i >= nvec) break;
       if constexpr (DT == FP8Q_F32) {
         const uint32_t mv = vec_absmax<DT>(0u, v[u]);
@@ -247,7 +251,7 @@ __device__ __forceinline__ uint32_t tensor_stream(const u32x4* __restrict__ xv, 
 }
 
 template <int DT, int FMT, int ODT>
-__global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restrict__ x, int64_t n,
+__global__ __launch_bounds__(FP8Q_TH_T) void k_quant_tensor(const void* __restrict__ x, int64_t n,
                                                            const float* __restrict__ scale,
                                                            uint8_t* __restrict__ q,
                                                            uint32_t* __restrict__ amax_acc,
@@ -260,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restric
   uint32_t m = scale_ok(s) ? tensor_stream<DT, FMT, true, ODT>(xv, nvec, s, r, q, y)
                            : tensor_stream<DT, FMT, false, ODT>(xv, nvec, s, r, q, y);
   if (blockIdx.x == 0) {
-    for (int64_t j = nvec * per_vec + threadIdx.x; j < n; j += kThreads) {
+    for (int64_t j = nvec * per_vec + threadIdx.x; j < n; j += FP8Q_TH_T) {
       uint32_t b = DT == FP8Q_F32 ? ((const uint32_t*)x)[j]
                                   : (uint32_t)((const uint16_t*)x)[j] << 16;
       m = max(m, b & 0x7FFFFFFFu);
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_tensor(const void* __restric
     }
   }
   if (amax_acc) {
-    m = block_max(m);
+    m = block_max<FP8Q_TH_T>(m);
     if (threadIdx.x == 0) fold_max(amax_acc, canon_abs_bits(m));
   }
 }
@@ -892,13 +896,13 @@ template <int DT, int FMT>
 static void launch_qt(int grid, const void* x, int64_t n, const float* scale, uint8_t* q,
                       float* amax_acc, hipStream_t st, void* y = nullptr, int out_dt = -1) {
   if (out_dt == FP8Q_F32)
-    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, FP8Q_F32>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, FP8Q_F32>), dim3(grid), dim3(FP8Q_TH_T), 0, st, x, n, scale, q,
                        (uint32_t*)amax_acc, y);
   else if (out_dt == FP8Q_BF16)
-    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, FP8Q_BF16>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, FP8Q_BF16>), dim3(grid), dim3(FP8Q_TH_T), 0, st, x, n, scale, q,
                        (uint32_t*)amax_acc, y);
   else
-    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, -1>), dim3(grid), dim3(kThreads), 0, st, x, n, scale, q,
+    hipLaunchKernelGGL((k_quant_tensor<DT, FMT, -1>), dim3(grid), dim3(FP8Q_TH_T), 0, st, x, n, scale, q,
                        (uint32_t*)amax_acc, y);
 }
 
@@ -911,7 +915,7 @@ int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const floa
     if (int e = check_launch("quantize_tensor amax reset")) return e;
   }
   const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
-  const int64_t ch = (int64_t)FP8Q_KU_T * kThreads;
+  const int64_t ch = (int64_t)FP8Q_KU_T * FP8Q_TH_T;
   const int grid = chunk_grid((nvec + ch - 1) / ch, FP8Q_G_T);
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN)
     launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax, st, y, out_dt);
