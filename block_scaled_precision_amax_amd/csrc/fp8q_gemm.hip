@@ -873,6 +873,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
     uint8_t* dst = sc_a ? lds_sa[st] + 256 * (wave & 3) : lds_sb[st] + 256 * (wave & 3);
     lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
   };
+  // copy p (0-3 A, 4-7 B, 8 the scale bytes) of block kb into stage st
+  auto stage_part = [&](int64_t kb, int st, int p) {
+    if (p < 4) {
+      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_a[st] + (wave * 4 + p) * 1024)), A + kb * BK, a_off[p]);
+    } else if (p < 8) {
+      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_b[st] + (wave * 4 + p - 4) * 1024)), B + kb * BK,
+                b_off[p - 4]);
+    } else {
+      uint8_t* dst = sc_a ? lds_sa[st] + 256 * (wave & 3) : lds_sb[st] + 256 * (wave & 3);
+      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
+    }
+  };
 
   // B fragments and scales of the block being computed; A fragments and
   // scales of two row tiles (the one computed and the next), by parity.
@@ -898,12 +910,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
                                                                 sai[i & 1]);
   };
   // row tiles 0 .. TI-2 of a block, each with the next row tile's A read
-  auto rows = [&](int st) {
+  auto rows = [&](int st, int64_t kbn) {
 #pragma unroll
     for (int i = 0; i + 1 < TI; ++i) {
       load_a(st, i + 1);
 #pragma unroll
-      for (int j = 0; j < TJ; ++j) mma(i, j);
+      for (int j = 0; j < TJ; ++j) {
+        mma(i, j);
+        if (j == 0 && i < 5) stage_part(kbn, st ^ 1, 4 + i);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -911,36 +926,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
 
   // Software pipeline over K blocks (two LDS stages, block kb in stage
   // kb % 2).  The barrier that publishes block kb sits before the last row
-  // tile of block kb-1; right after it the copy of block kb+1 goes into the
-  // stage block kb-1 has finished with, and the fragments of block kb are
+  // tile of block kb-1; after it the nine copies of block kb+1 go into the
+  // stage block kb-1 has finished with, one after each of the last row
+  // tile's MFMAs and one per row tile after that (a copy stalls the
+  // wavefront that issues it; spread out, the stalls fall between MFMAs
+  // instead of all at the block start), and the fragments of block kb are
   // read behind the last row tile's MFMAs, so no block starts by waiting
   // for its first LDS reads.  One pass of the loop is the last row tile of
-  // block kb-1 followed by the other row tiles of block kb.
+  // block kb-1 followed by the other row tiles of block kb.  The copies
+  // carry no condition: the last pass copies block nkb-1 once more, into
+  // the stage nothing reads any more.
   stage_block(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (nkb > 1) stage_block(1, 1);
+  {
+    // block 1 (block 0 again when there is one block: stage 1 is then never read)
+    const int64_t k1 = nkb > 1 ? 1 : 0;
 #pragma unroll
-  for (int j = 0; j < TJ; ++j) load_b(0, j);
-  load_a(0, 0);
-  rows(0);
+    for (int p = 0; p < 4; ++p) stage_part(k1, 1, p);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) load_b(0, j);
+    load_a(0, 0);
+    rows(0, k1);
+  }
   for (int64_t kb = 1; kb < nkb; ++kb) {
     const int st = (int)(kb & 1);
     // every lane's reads of stage st^1 are done and block kb has landed
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kb + 1 < nkb) stage_block(kb + 1, st ^ 1);
+    const int64_t kbn = kb + 1 < nkb ? kb + 1 : nkb - 1;
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       mma(TI - 1, j);
+      stage_part(kbn, st ^ 1, j);
       load_b(st, j);
       __builtin_amdgcn_sched_barrier(0);
     }
     load_a(st, 0);
-    rows(st);
+    rows(st, kbn);
   }
 #pragma unroll
   for (int j = 0; j < TJ; ++j) mma(TI - 1, j);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue
   constexpr int WB = TI * 16 * TJ * 16 * 2;
