@@ -255,6 +255,21 @@ def run_gpu(steps: int, warmup: int):
                                                                         LK, sW, fq.GRAN_128x128, LK // 128, 1, C, LN, LM,
                                                                         LN, LK), 4),
     }
+    # the remaining quantizer rows: 128x128 blocks of the activation, amax
+    # alone, and current scaling (amax, the scale from it, the quantize: two
+    # reads and one write of the tensor)
+    sX128 = torch.empty(LM // 128, LK // 128, dtype=torch.float32, device=dev)
+    per["quantize_128x128"] = per_launch(lambda r: fq.fp8q_quantize_128x128(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, 1e-12,
+                                                                             qX, LK, sX128, LK // 128), 8)
+    per["amax_x"] = per_launch(lambda r: fq.fp8q_amax(xs[r % N_ROT], n, am_tmp), 16)
+    st_w1 = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
+    fq.fp8q_delayed_scaler_init(st_w1, 1, 448.0, 1e-12, 1.0)
+
+    def current_scaling(r):
+        fq.fp8q_amax(xs[r % N_ROT], n, am_tmp)
+        fq.fp8q_delayed_scaler_update(st_w1, am_tmp)  # window 1: s = amax / 448
+        fq.fp8q_quantize_tensor_delayed(xs[r % N_ROT], n, fq.E4M3FN, st_w1, qx)
+    per["current_scaling_x"] = per_launch(current_scaling, 8)
     # the same GEMM with its output quantized 1x128 (E4M3FN) in the epilogue
     qC = torch.empty(LM, LN, dtype=torch.uint8, device=dev)
     sC = torch.empty(LM, LN // 128, dtype=torch.float32, device=dev)
@@ -609,6 +624,19 @@ def main():
             "quantize_tensor_dq_bf16_e4m3": {"ms": round(per["quantize_tensor_dq_x"], 4), "GB/s": round(q_dq, 1),
                                              "frac_hbm": round(q_dq / HBM_PEAK_GBPS, 4), "frac_stream": fs(q_dq, "copy"),
                                              "note": "codes and their bf16 round trip in one pass (the step's x)"},
+            "quantize_128x128_bf16": {
+                "ms": round(per["quantize_128x128"], 4),
+                "GB/s": round(gbps(LM * LK * (3 + 4 / 16384), per["quantize_128x128"]), 1),
+                "frac_hbm": round(gbps(LM * LK * (3 + 4 / 16384), per["quantize_128x128"]) / HBM_PEAK_GBPS, 4),
+                "frac_stream": fs(gbps(LM * LK * (3 + 4 / 16384), per["quantize_128x128"]), "bf16_to_codes"),
+                "note": "128x128 blocks of the layer's activation 16384x7168"},
+            "amax_bf16": {"ms": round(per["amax_x"], 4), "GB/s": round(gbps(2 * DS_ROWS * DS_COLS, per["amax_x"]), 1),
+                          "frac_hbm": round(gbps(2 * DS_ROWS * DS_COLS, per["amax_x"]) / HBM_PEAK_GBPS, 4),
+                          "note": "fp8q_amax alone over the 8192x8192 bf16 tensor (one read)"},
+            "current_scaling_bf16_e4m3": {
+                "ms": round(per["current_scaling_x"], 4), "GB/s": round(gbps(5 * DS_ROWS * DS_COLS, per["current_scaling_x"]), 1),
+                "frac_hbm": round(gbps(5 * DS_ROWS * DS_COLS, per["current_scaling_x"]) / HBM_PEAK_GBPS, 4),
+                "note": "current scaling: amax, the scale from it, then the quantize (two reads + one write)"},
             "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
                                 "frac_hbm": round(dq / HBM_PEAK_GBPS, 4),
                                 "frac_stream": fs(dq, "codes_to_bf16")},
