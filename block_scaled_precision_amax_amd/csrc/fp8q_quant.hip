@@ -408,33 +408,36 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict
 // ---------------------------------------------------------------- 1x128 of the transpose
 // x [rows, cols] -> the codes of x^T [cols, rows], one scale per 128 rows of
 // a column of x (a 1x128 block of x^T: the layout the weight-gradient GEMM
-// takes for operands reduced over tokens).  A workgroup takes a 64-column
-// slab of x and walks FP8Q_RT consecutive 128-row blocks of it, loading the
-// next block while it encodes the current one.  Each 128x64 tile is staged
-// in LDS in its input type with the column index XORed by
-// 16*((row/16) mod 4), which keeps the row-wise staging writes and the
-// column-wise reads free of bank conflicts.  The four lanes of a quad hold
-// one column's 128 values, reduce its amax with two shuffles and write its
-// 128 codes as one contiguous run of the transposed output.
+// takes for operands reduced over tokens).  A workgroup of 4W threads takes
+// a W-column slab of x (W = 128 when the column count allows, else 64) and
+// walks FP8Q_RT consecutive 128-row blocks of it, loading the next block
+// while it encodes the current one; each load instruction reads 256-byte
+// (bf16, W = 128) pieces of four rows.  Each 128xW tile is staged in LDS in
+// its input type with the column index XORed by 16*((row/16) mod 4), which
+// keeps the row-wise staging writes and the column-wise reads free of bank
+// conflicts.  The four lanes of a quad hold one column's 128 values, reduce
+// its amax with two shuffles and write its 128 codes as one contiguous run
+// of the transposed output.
 #ifndef FP8Q_RT
-#define FP8Q_RT 16  // row blocks per workgroup in the transposed quantizer (measured)
+#define FP8Q_RT 8  // row blocks per workgroup in the transposed quantizer (measured)
 #endif
-template <int DT, int FMT>
-__global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restrict__ x, int64_t ntc,
+template <int DT, int FMT, int W>
+__global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict__ x, int64_t ntc,
                                                             int64_t nrb, int64_t ldx, float eps,
                                                             uint8_t* __restrict__ q, int64_t ldq,
                                                             float* __restrict__ scales, int64_t ld_s) {
-  // bf16 stays bf16 in LDS (16 KB per workgroup)
-  __shared__ __attribute__((aligned(16))) uint32_t tile_raw[DT == FP8Q_F32 ? 128 * 64 : 128 * 32];
+  // bf16 stays bf16 in LDS (32 KB per workgroup at W = 128)
+  __shared__ __attribute__((aligned(16))) uint32_t tile_raw[DT == FP8Q_F32 ? 128 * W : 128 * W / 2];
+  constexpr int TH = 4 * W;
   float* tile = (float*)tile_raw;
   uint16_t* tile16 = (uint16_t*)tile_raw;
   constexpr int esz = DT == FP8Q_F32 ? 4 : 2;
   constexpr int VE = 16 / esz;                 // elements per 16-byte vector
-  constexpr int VPR = 64 / VE;                 // vectors per tile row
-  constexpr int NVT = 128 * VPR / kThreads;    // vectors per thread
-  // workgroup -> (group of FP8Q_RT row blocks, 64-column slab)
+  constexpr int VPR = W / VE;                  // vectors per tile row
+  constexpr int NVT = 128 * VPR / TH;          // vectors per thread
+  // workgroup -> (group of FP8Q_RT row blocks, W-column slab)
   const int64_t cb = blockIdx.x % ntc, rg = blockIdx.x / ntc;
-  const int64_t c0 = cb * 64;
+  const int64_t c0 = cb * W;
   const int64_t rb_begin = rg * FP8Q_RT;
   const int64_t rb_end = rb_begin + FP8Q_RT < nrb ? rb_begin + FP8Q_RT : nrb;
   const int tid = threadIdx.x;
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restri
   auto load = [&](int64_t rb, u32x4* v) {
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
-      const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
+      const int vi = tid + i * TH, t = vi / VPR, c = (vi % VPR) * VE;
       v[i] = __builtin_nontemporal_load((const u32x4*)(xb + ((rb * 128 + t) * ldx + c0 + c) * esz));
     }
   };
@@ -457,11 +460,11 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restri
   auto block = [&](int64_t rb, const u32x4* v) {
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
-      const int vi = tid + i * kThreads, t = vi / VPR, c = (vi % VPR) * VE;
+      const int vi = tid + i * TH, t = vi / VPR, c = (vi % VPR) * VE;
       if constexpr (DT == FP8Q_F32)
-        *(u32x4*)(tile + t * 64 + (c ^ swz(t))) = v[i];
+        *(u32x4*)(tile + t * W + (c ^ swz(t))) = v[i];
       else
-        *(u32x4*)(tile16 + t * 64 + (c ^ swz(t))) = v[i];
+        *(u32x4*)(tile16 + t * W + (c ^ swz(t))) = v[i];
     }
     __syncthreads();
     float a[32];
@@ -470,9 +473,9 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128_t(const void* __restri
     for (int j = 0; j < 32; ++j) {
       const int t = 16 * k + (j & 15) + 64 * (j >> 4);  // swz(t) == 16k
       if constexpr (DT == FP8Q_F32)
-        a[j] = tile[t * 64 + fc];
+        a[j] = tile[t * W + fc];
       else
-        a[j] = __uint_as_float((uint32_t)tile16[t * 64 + fc] << 16);
+        a[j] = __uint_as_float((uint32_t)tile16[t * W + fc] << 16);
       m = max(m, __float_as_uint(a[j]) & 0x7FFFFFFFu);
     }
     __syncthreads();  // the tile is rewritten by the next row block
@@ -950,22 +953,27 @@ int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int
 }
 
 template <int DT, int FMT>
-static void launch_q1t(int64_t wgs, const void* x, int64_t ntc, int64_t nrb, int64_t ldx, float eps, uint8_t* q,
+static void launch_q1t(int64_t ngr, const void* x, int64_t ntc, int64_t nrb, int64_t ldx, float eps, uint8_t* q,
                        int64_t ldq, float* scales, int64_t ld_s, hipStream_t st) {
-  hipLaunchKernelGGL((k_quant_1x128_t<DT, FMT>), dim3((unsigned)wgs), dim3(kThreads), 0, st, x, ntc, nrb, ldx, eps,
-                     q, ldq, scales, ld_s);
+  // ntc 64-column slabs; 128-column slabs when they pair up
+  if (ntc % 2 == 0)
+    hipLaunchKernelGGL((k_quant_1x128_t<DT, FMT, 128>), dim3((unsigned)(ngr * (ntc / 2))), dim3(512), 0, st, x,
+                       ntc / 2, nrb, ldx, eps, q, ldq, scales, ld_s);
+  else
+    hipLaunchKernelGGL((k_quant_1x128_t<DT, FMT, 64>), dim3((unsigned)(ngr * ntc)), dim3(256), 0, st, x, ntc, nrb,
+                       ldx, eps, q, ldq, scales, ld_s);
 }
 
 int launch_quantize_1x128_t(const void* x, int dt, int64_t rows, int64_t cols, int64_t ldx, int fmt,
                             float eps, uint8_t* q, int64_t ldq, float* scales, int64_t ld_s,
                             hipStream_t st) {
   const int64_t ntc = cols / 64, nrb = rows / 128;
-  const int64_t wgs = ((nrb + FP8Q_RT - 1) / FP8Q_RT) * ntc;
-  if (wgs > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "quantize_1x128_t: more than 2^31-1 workgroups");
-  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_F32, FP8Q_E4M3FN>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
-  else if (dt == FP8Q_F32) launch_q1t<FP8Q_F32, FP8Q_E5M2>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
-  else if (fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_BF16, FP8Q_E4M3FN>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
-  else launch_q1t<FP8Q_BF16, FP8Q_E5M2>(wgs, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  const int64_t ngr = (nrb + FP8Q_RT - 1) / FP8Q_RT;  // row-block groups
+  if (ngr * ntc > 0x7FFFFFFF) return fail(FP8Q_ESHAPE, "quantize_1x128_t: more than 2^31-1 workgroups");
+  if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_F32, FP8Q_E4M3FN>(ngr, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (dt == FP8Q_F32) launch_q1t<FP8Q_F32, FP8Q_E5M2>(ngr, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  else if (fmt == FP8Q_E4M3FN) launch_q1t<FP8Q_BF16, FP8Q_E4M3FN>(ngr, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
+  else launch_q1t<FP8Q_BF16, FP8Q_E5M2>(ngr, x, ntc, nrb, ldx, eps, q, ldq, scales, ld_s, st);
   return check_launch("quantize_1x128_t");
 }
 

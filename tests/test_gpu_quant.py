@@ -416,10 +416,12 @@ def oracle_t(orc, x_np, fmt):
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("rows,cols,ldx,pad_q", [(128, 64, 64, 0), (256, 192, 200, 32), (384, 128, 136, 16),
-                                                 (128, 1024, 1024, 0), (384, 512, 520, 16), (640, 768, 768, 0)])
+                                                 (128, 1024, 1024, 0), (384, 512, 520, 16), (640, 768, 768, 0),
+                                                 (1280, 256, 264, 16), (1152, 320, 320, 0)])
 def test_quantize_1x128_t(fq, orc, gpu, dt, fmt, rows, cols, ldx, pad_q):
-    """Padded rows, one and several 64-column slabs, several 128-row blocks
-    per workgroup."""
+    """Padded rows; one or an odd number of 64-column slabs (64-column
+    workgroups) and pairs of them (128-column workgroups); several 128-row
+    blocks per workgroup, and a last workgroup with fewer row blocks."""
     rng = np.random.default_rng(rows + cols + fmt)
     x = (rng.standard_normal((rows, ldx)) * np.exp(rng.standard_normal((1, ldx)) * 3)).astype(np.float32)
     xd = torch.from_numpy(x).to(dt).to(gpu)
