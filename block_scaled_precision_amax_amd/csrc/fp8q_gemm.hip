@@ -26,7 +26,10 @@
 // wavefront 64x64) on the exact path.  Per 128-wide K block the A and B
 // code tiles are copied into LDS by the global-to-LDS load path (two stages
 // on the FP8 paths, three on the exact path), with an XOR chunk swizzle
-// that keeps the fragment reads free of bank conflicts.  The A scales of
+// that keeps the fragment reads free of bank conflicts.  A copy instruction
+// stalls the wavefront that issues it for tens of cycles, so only
+// wavefronts 0-3 issue them (each its own share and that of wavefront w+4,
+// which runs on the same SIMD and keeps issuing MFMAs meanwhile).  The A scales of
 // the tile's rows travel with the codes, so promotion is one FMA per output
 // element and K block.  The MFMAs take B as their first operand, so each
 // lane holds one row and four consecutive columns of C, and C leaves
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   // with 1x128 B scales, those of the tile's columns
   constexpr bool SB_COLS = GB == FP8Q_GRAN_1x128;
   __shared__ __attribute__((aligned(16))) float lds_sb[NST][SB_COLS ? BN : 1];
-  constexpr int NL = G::NLOAD + (SB_COLS ? 1 : 0);  // loads per wavefront per K block
+  constexpr int NL = G::NLOAD + (SB_COLS ? 1 : 0);  // loads per wavefront share per K block
   // quantized outputs: each wavefront's row maxima, read by its neighbour,
   // and its column maxima, read by its partner in the 128-row block
   __shared__ uint32_t lds_rmax[ODT >= kOutQ ? 8 * TI * 16 : 1];
@@ -519,9 +522,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int sa_p = wave * SA_LANES + (lane < SA_LANES ? lane : 0);
   const int64_t sa_r = m0 + (sa_p / (16 * TI)) * 16 * TI + 16 * (sa_p % TI) + (sa_p % (16 * TI)) / TI;
   const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
-  uint32_t a_off[BM / 64], b_off[BN / 64];
+  const int sa_p2 = (wave + 4) * SA_LANES + (lane < SA_LANES ? lane : 0);
+  const int64_t sa_r2 = m0 + (sa_p2 / (16 * TI)) * 16 * TI + 16 * (sa_p2 % TI) + (sa_p2 % (16 * TI)) / TI;
+  const float* sa_row2 = sA + (sa_r2 < M ? sa_r2 : M - 1) * sA_sm;
+  uint32_t a_off[BM / 64], b_off[BN / 64], a_off2[BM / 64], b_off2[BN / 64];
   dma_offsets<BM, true>(a_off, lda, m0, M, wave, lane);
   dma_offsets<BN, true>(b_off, ldb, n0, N, wave, lane);
+  dma_offsets<BM, true>(a_off2, lda, m0, M, wave + 4, lane);
+  dma_offsets<BN, true>(b_off2, ldb, n0, N, wave + 4, lane);
 
   v4f acc[TI][TJ];
 #pragma unroll
@@ -541,6 +549,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   constexpr int SB_LANES = BN / 8;
   const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);
   const float* sb_col = sB + (sb_c < N ? sb_c : N - 1) * sB_sn;
+  const int64_t sb_c2 = n0 + (wave + 4) * SB_LANES + (lane < SB_LANES ? lane : 0);
+  const float* sb_col2 = sB + (sb_c2 < N ? sb_c2 : N - 1) * sB_sn;
 
   // P_kb of every MFMA tile of the wavefront, folded into acc.  The MFMAs
   // take the B fragment as their first operand and the A fragment as their
@@ -667,7 +677,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
             if (wait_all)
               asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             else
-              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
             __syncthreads();
             const uint8_t* lbn = lds_b[nxt] + b_row0;
 #pragma unroll
@@ -716,14 +726,23 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   };
 
   // Everything one wavefront copies into LDS stage st for K block kb.
+  // wavefronts 0-3 copy their share and that of wavefront w+4 (2*NL loads);
+  // the others copy nothing, so every wait below allows 2*NL in flight
   auto stage_block = [&](int64_t kb, int st) {
+    if (wm != 0) return;
     dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
     dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
-    if (lane < SA_LANES)
+    dma_tile<BM>(lds_a[st], A + kb * BK, a_off2, wave + 4);
+    dma_tile<BN>(lds_b[st], B + kb * BK, b_off2, wave + 4);
+    if (lane < SA_LANES) {
       lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + (wave + 4) * SA_LANES)), sa_row2 + kb * sA_skb);
+    }
     if constexpr (SB_COLS) {
-      if (lane < SB_LANES)
+      if (lane < SB_LANES) {
         lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + wave * SB_LANES)), sb_col + kb * sB_skb);
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + (wave + 4) * SB_LANES)), sb_col2 + kb * sB_skb);
+      }
     }
   };
   auto next_stage = [](int st) { return st + 1 == NST ? 0 : st + 1; };
@@ -733,7 +752,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   if constexpr (NST == 3) {
     if (nkb > 1) {
       stage_block(1, 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
