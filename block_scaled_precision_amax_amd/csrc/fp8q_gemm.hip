@@ -842,9 +842,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
 // registers and 64+16q .. 64+16q+16 in the last four, and the scale from
 // lane group g covers K positions 32g .. 32g+32 (measured on gfx950): each
 // lane therefore reads 16-byte chunks q and q+4 of its row, which keeps K
-// in memory order, and passes the scale of the 32-block g = q.  Tiling,
-// copies and tile order are those of the FP8 path (256x256 workgroup tile,
-// two LDS stages); the scale bytes of the tile's rows and columns (4 per
+// in memory order, and passes the scale of the 32-block g = q.  Tiling
+// and tile order are those of the FP8 path (256x256 workgroup tile, two LDS
+// stages); every wavefront copies its share of each block, spread over the
+// MFMAs (below), and the scale bytes of the tile's rows and columns (4 per
 // row and 128-wide K block) travel through LDS with the codes.
 template <int FA, int FB, int ODT>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
