@@ -522,14 +522,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   const int sa_p = wave * SA_LANES + (lane < SA_LANES ? lane : 0);
   const int64_t sa_r = m0 + (sa_p / (16 * TI)) * 16 * TI + 16 * (sa_p % TI) + (sa_p % (16 * TI)) / TI;
   const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
+  // With 128x128 B scales, wavefronts 0-3 copy their share of each block and
+  // that of wavefront w+4 (below); with 1x128 B scales every wavefront copies
+  // its own (the partner's offsets would not fit in the registers).
+  constexpr bool PAIRCOPY = !SB_COLS;
+  constexpr int NW = PAIRCOPY ? 2 * NL : NL;  // copies per wavefront and K block
   const int sa_p2 = (wave + 4) * SA_LANES + (lane < SA_LANES ? lane : 0);
   const int64_t sa_r2 = m0 + (sa_p2 / (16 * TI)) * 16 * TI + 16 * (sa_p2 % TI) + (sa_p2 % (16 * TI)) / TI;
   const float* sa_row2 = sA + (sa_r2 < M ? sa_r2 : M - 1) * sA_sm;
   uint32_t a_off[BM / 64], b_off[BN / 64], a_off2[BM / 64], b_off2[BN / 64];
   dma_offsets<BM, true>(a_off, lda, m0, M, wave, lane);
   dma_offsets<BN, true>(b_off, ldb, n0, N, wave, lane);
-  dma_offsets<BM, true>(a_off2, lda, m0, M, wave + 4, lane);
-  dma_offsets<BN, true>(b_off2, ldb, n0, N, wave + 4, lane);
+  if constexpr (PAIRCOPY) {
+    dma_offsets<BM, true>(a_off2, lda, m0, M, wave + 4, lane);
+    dma_offsets<BN, true>(b_off2, ldb, n0, N, wave + 4, lane);
+  }
 
   v4f acc[TI][TJ];
 #pragma unroll
@@ -549,8 +556,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   constexpr int SB_LANES = BN / 8;
   const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);
   const float* sb_col = sB + (sb_c < N ? sb_c : N - 1) * sB_sn;
-  const int64_t sb_c2 = n0 + (wave + 4) * SB_LANES + (lane < SB_LANES ? lane : 0);
-  const float* sb_col2 = sB + (sb_c2 < N ? sb_c2 : N - 1) * sB_sn;
 
   // P_kb of every MFMA tile of the wavefront, folded into acc.  The MFMAs
   // take the B fragment as their first operand and the A fragment as their
@@ -677,7 +682,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
             if (wait_all)
               asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             else
-              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NW) : "memory");
             __syncthreads();
             const uint8_t* lbn = lds_b[nxt] + b_row0;
 #pragma unroll
@@ -726,23 +731,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   };
 
   // Everything one wavefront copies into LDS stage st for K block kb.
-  // wavefronts 0-3 copy their share and that of wavefront w+4 (2*NL loads);
-  // the others copy nothing, so every wait below allows 2*NL in flight
+  // PAIRCOPY: wavefronts 0-3 copy their share and that of wavefront w+4
+  // (2*NL loads) and the others copy nothing; otherwise each copies its NL.
+  // Every wait allows NW loads in flight.
   auto stage_block = [&](int64_t kb, int st) {
-    if (wm != 0) return;
-    dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
-    dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
-    dma_tile<BM>(lds_a[st], A + kb * BK, a_off2, wave + 4);
-    dma_tile<BN>(lds_b[st], B + kb * BK, b_off2, wave + 4);
-    if (lane < SA_LANES) {
-      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
-      lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + (wave + 4) * SA_LANES)), sa_row2 + kb * sA_skb);
-    }
-    if constexpr (SB_COLS) {
-      if (lane < SB_LANES) {
-        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + wave * SB_LANES)), sb_col + kb * sB_skb);
-        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + (wave + 4) * SB_LANES)), sb_col2 + kb * sB_skb);
+    if constexpr (PAIRCOPY) {
+      if (wm != 0) return;
+      dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+      dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
+      dma_tile<BM>(lds_a[st], A + kb * BK, a_off2, wave + 4);
+      dma_tile<BN>(lds_b[st], B + kb * BK, b_off2, wave + 4);
+      if (lane < SA_LANES) {
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + (wave + 4) * SA_LANES)),
+                 sa_row2 + kb * sA_skb);
       }
+    } else {
+      dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+      dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
+      if (lane < SA_LANES)
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+      if (lane < SB_LANES)
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + wave * SB_LANES)), sb_col + kb * sB_skb);
     }
   };
   auto next_stage = [](int st) { return st + 1 == NST ? 0 : st + 1; };
@@ -752,7 +762,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   if constexpr (NST == 3) {
     if (nkb > 1) {
       stage_block(1, 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NL) : "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NW) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
