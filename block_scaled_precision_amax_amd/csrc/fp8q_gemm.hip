@@ -27,9 +27,10 @@
 // code tiles are copied into LDS by the global-to-LDS load path (two stages
 // on the FP8 paths, three on the exact path), with an XOR chunk swizzle
 // that keeps the fragment reads free of bank conflicts.  A copy instruction
-// stalls the wavefront that issues it for tens of cycles, so only
-// wavefronts 0-3 issue them (each its own share and that of wavefront w+4,
-// which runs on the same SIMD and keeps issuing MFMAs meanwhile).  The A scales of
+// stalls the wavefront that issues it for tens of cycles, so with 128x128 B
+// scales only wavefronts 0-3 issue them (each its own share and that of
+// wavefront w+4, which runs on the same SIMD and keeps issuing MFMAs
+// meanwhile).  The A scales of
 // the tile's rows travel with the codes, so promotion is one FMA per output
 // element and K block.  The MFMAs take B as their first operand, so each
 // lane holds one row and four consecutive columns of C, and C leaves
