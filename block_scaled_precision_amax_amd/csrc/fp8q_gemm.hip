@@ -34,9 +34,10 @@
 // the tile's rows travel with the codes, so promotion is one FMA per output
 // element and K block.  The MFMAs take B as their first operand, so each
 // lane holds one row and four consecutive columns of C, and C leaves
-// through LDS in whole row pieces.  Workgroups are renumbered so that each
-// of the eight XCDs (one L2 each) walks a contiguous, M-grouped part of the
-// tile grid.
+// through LDS in whole row pieces.  The grid is persistent (one workgroup
+// per compute unit, each walking tiles b, b + grid, ...), and tiles are
+// renumbered so that each of the eight XCDs (one L2 each) walks a
+// contiguous, M-grouped part of the tile grid.
 #include "fp8q_internal.h"
 
 #include <type_traits>
@@ -506,341 +507,351 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm(
   __shared__ uint32_t lds_rmax[ODT >= kOutQ ? 8 * TI * 16 : 1];
   __shared__ uint32_t lds_cmax[ODT >= kOutQT ? 8 * TJ * 16 : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  int64_t tm, tn;
-  tile_of(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t nkb = K / BK;
+  // Persistent grid: tiles blockIdx.x, + gridDim.x, ...  The lane and
+  // wavefront numbers are derived again for every tile (through an empty
+  // asm the compiler cannot see through): hoisted out of the tile loop,
+  // everything computed from them stays live across it and spills.
+  const int64_t ntiles = ntm * ntn;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    int64_t tm, tn;
+    tile_of(tile, ntiles, ntm, ntn, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t nkb = K / BK;
 
-  // A scales: wavefront w stages rows w*BM/8 .. +BM/8 of the tile, one per
-  // lane (rows past M read the last row)
-  // In LDS the scales are ordered so that the TI scales one lane needs
-  // (rows 16i + lr of its wavefront half, i = 0..TI-1) are contiguous: slot
-  // p = h*16TI + lr*TI + i holds row h*16TI + 16i + lr.
-  constexpr int SA_LANES = BM / 8;
-  const int sa_p = wave * SA_LANES + (lane < SA_LANES ? lane : 0);
-  const int64_t sa_r = m0 + (sa_p / (16 * TI)) * 16 * TI + 16 * (sa_p % TI) + (sa_p % (16 * TI)) / TI;
-  const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
-  // With 128x128 B scales, wavefronts 0-3 copy their share of each block and
-  // that of wavefront w+4 (below); with 1x128 B scales every wavefront copies
-  // its own (the partner's offsets would not fit in the registers).
-  constexpr bool PAIRCOPY = !SB_COLS;
-  constexpr int NW = PAIRCOPY ? 2 * NL : NL;  // copies per wavefront and K block
-  const int sa_p2 = (wave + 4) * SA_LANES + (lane < SA_LANES ? lane : 0);
-  const int64_t sa_r2 = m0 + (sa_p2 / (16 * TI)) * 16 * TI + 16 * (sa_p2 % TI) + (sa_p2 % (16 * TI)) / TI;
-  const float* sa_row2 = sA + (sa_r2 < M ? sa_r2 : M - 1) * sA_sm;
-  uint32_t a_off[BM / 64], b_off[BN / 64], a_off2[BM / 64], b_off2[BN / 64];
-  dma_offsets<BM, true>(a_off, lda, m0, M, wave, lane);
-  dma_offsets<BN, true>(b_off, ldb, n0, N, wave, lane);
-  if constexpr (PAIRCOPY) {
-    dma_offsets<BM, true>(a_off2, lda, m0, M, wave + 4, lane);
-    dma_offsets<BN, true>(b_off2, ldb, n0, N, wave + 4, lane);
-  }
-
-  v4f acc[TI][TJ];
-#pragma unroll
-  for (int i = 0; i < TI; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-  // 16x16 results: column l%16, rows 4*(l/16) + e.  Operand fragments: row
-  // (A) / column (B) l%16 and K bytes chosen by l/16 (the same K for A and B).
-  const int lr = lane & 15, lq = lane >> 4;
-  const int a_row0 = (wm * TI * 16 + lr) * BK, b_row0 = (wn * TJ * 16 + lr) * BK;
-  const int64_t wcol0 = n0 + wn * TJ * 16;  // first column of this wavefront
-  // its 128x128 B-scale row; a wavefront wholly past column N (its results
-  // are never stored) reads the last row instead of one past the array
-  const float* sb_blk = sB + ((wcol0 < N ? wcol0 : N - 1) >> 7) * sB_sn;
-  // 1x128 B scales: wavefront w stages columns w*BN/8 .. +BN/8 of the tile
-  constexpr int SB_LANES = BN / 8;
-  const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);
-  const float* sb_col = sB + (sb_c < N ? sb_c : N - 1) * sB_sn;
-
-  // P_kb of every MFMA tile of the wavefront, folded into acc.  The MFMAs
-  // take the B fragment as their first operand and the A fragment as their
-  // second, so a 16x16 result holds C transposed: lane (lr, lq) gets row
-  // 16i + lr and columns 16j + 4lq + e.  A lane then needs one A scale per
-  // row tile (not four), and its four results of a tile are consecutive
-  // columns of one row.
-  // Exact path: the decoded B fragments of the block being computed and the
-  // decoded A fragment of its first row tile, carried from one block to the
-  // next (decoded while the previous block's last row tile runs).
-  constexpr bool H16X = FA == FP8Q_E5M2 || FB == FP8Q_E5M2;
-  typename Mf<H16X>::v8 xfb[TJ][4], xfa[4];
-  // compute(kb, s, pf, nxt, wait_all): with pf true (a compile-time tag) the
-  // block also publishes block kb+1 (stage nxt) and decodes its first
-  // fragments; wait_all says no newer copy is in flight.
-  auto compute = [&](int64_t kb, int s, auto pf_tag, int nxt, bool wait_all) {
-    constexpr bool PF = decltype(pf_tag)::value;
-    // the B scale(s) of this wavefront's columns
-    v4f sbv[TJ];
-    float sbw = 1.0f;
-    if constexpr (GB == FP8Q_GRAN_128x128) {
-      sbw = sb_blk[kb * sB_skb];
-    } else {
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) {
-        const float4 t = *(const float4*)(lds_sb[s] + wn * TJ * 16 + 16 * j + 4 * lq);
-        sbv[j] = v4f{t.x, t.y, t.z, t.w};
-      }
+    // A scales: wavefront w stages rows w*BM/8 .. +BM/8 of the tile, one per
+    // lane (rows past M read the last row)
+    // In LDS the scales are ordered so that the TI scales one lane needs
+    // (rows 16i + lr of its wavefront half, i = 0..TI-1) are contiguous: slot
+    // p = h*16TI + lr*TI + i holds row h*16TI + 16i + lr.
+    constexpr int SA_LANES = BM / 8;
+    const int sa_p = wave * SA_LANES + (lane < SA_LANES ? lane : 0);
+    const int64_t sa_r = m0 + (sa_p / (16 * TI)) * 16 * TI + 16 * (sa_p % TI) + (sa_p % (16 * TI)) / TI;
+    const float* sa_row = sA + (sa_r < M ? sa_r : M - 1) * sA_sm;
+    // With 128x128 B scales, wavefronts 0-3 copy their share of each block and
+    // that of wavefront w+4 (below); with 1x128 B scales every wavefront copies
+    // its own (the partner's offsets would not fit in the registers).
+    constexpr bool PAIRCOPY = !SB_COLS;
+    constexpr int NW = PAIRCOPY ? 2 * NL : NL;  // copies per wavefront and K block
+    const int sa_p2 = (wave + 4) * SA_LANES + (lane < SA_LANES ? lane : 0);
+    const int64_t sa_r2 = m0 + (sa_p2 / (16 * TI)) * 16 * TI + 16 * (sa_p2 % TI) + (sa_p2 % (16 * TI)) / TI;
+    const float* sa_row2 = sA + (sa_r2 < M ? sa_r2 : M - 1) * sA_sm;
+    uint32_t a_off[BM / 64], b_off[BN / 64], a_off2[BM / 64], b_off2[BN / 64];
+    dma_offsets<BM, true>(a_off, lda, m0, M, wave, lane);
+    dma_offsets<BN, true>(b_off, ldb, n0, N, wave, lane);
+    if constexpr (PAIRCOPY) {
+      dma_offsets<BM, true>(a_off2, lda, m0, M, wave + 4, lane);
+      dma_offsets<BN, true>(b_off2, ldb, n0, N, wave + 4, lane);
     }
-    const uint8_t* la = lds_a[s] + a_row0;
-    const uint8_t* lb = lds_b[s] + b_row0;
-    // the lane's TI A scales (times the block's B scale with 128x128 B scales)
-    float cf[TI];
-    {
-      const float* lc = lds_sa[s] + wm * TI * 16 + lr * TI;
+
+    v4f acc[TI][TJ];
 #pragma unroll
-      for (int q = 0; q < TI / 4; ++q) {
-        const float4 c4 = *(const float4*)(lc + 4 * q);
-        cf[4 * q] = c4.x;
-        cf[4 * q + 1] = c4.y;
-        cf[4 * q + 2] = c4.z;
-        cf[4 * q + 3] = c4.w;
-      }
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // 16x16 results: column l%16, rows 4*(l/16) + e.  Operand fragments: row
+    // (A) / column (B) l%16 and K bytes chosen by l/16 (the same K for A and B).
+    const int lr = lane & 15, lq = lane >> 4;
+    const int a_row0 = (wm * TI * 16 + lr) * BK, b_row0 = (wn * TJ * 16 + lr) * BK;
+    const int64_t wcol0 = n0 + wn * TJ * 16;  // first column of this wavefront
+    // its 128x128 B-scale row; a wavefront wholly past column N (its results
+    // are never stored) reads the last row instead of one past the array
+    const float* sb_blk = sB + ((wcol0 < N ? wcol0 : N - 1) >> 7) * sB_sn;
+    // 1x128 B scales: wavefront w stages columns w*BN/8 .. +BN/8 of the tile
+    constexpr int SB_LANES = BN / 8;
+    const int64_t sb_c = n0 + wave * SB_LANES + (lane < SB_LANES ? lane : 0);
+    const float* sb_col = sB + (sb_c < N ? sb_c : N - 1) * sB_sn;
+
+    // P_kb of every MFMA tile of the wavefront, folded into acc.  The MFMAs
+    // take the B fragment as their first operand and the A fragment as their
+    // second, so a 16x16 result holds C transposed: lane (lr, lq) gets row
+    // 16i + lr and columns 16j + 4lq + e.  A lane then needs one A scale per
+    // row tile (not four), and its four results of a tile are consecutive
+    // columns of one row.
+    // Exact path: the decoded B fragments of the block being computed and the
+    // decoded A fragment of its first row tile, carried from one block to the
+    // next (decoded while the previous block's last row tile runs).
+    constexpr bool H16X = FA == FP8Q_E5M2 || FB == FP8Q_E5M2;
+    typename Mf<H16X>::v8 xfb[TJ][4], xfa[4];
+    // compute(kb, s, pf, nxt, wait_all): with pf true (a compile-time tag) the
+    // block also publishes block kb+1 (stage nxt) and decodes its first
+    // fragments; wait_all says no newer copy is in flight.
+    auto compute = [&](int64_t kb, int s, auto pf_tag, int nxt, bool wait_all) {
+      constexpr bool PF = decltype(pf_tag)::value;
+      // the B scale(s) of this wavefront's columns
+      v4f sbv[TJ];
+      float sbw = 1.0f;
       if constexpr (GB == FP8Q_GRAN_128x128) {
-#pragma unroll
-        for (int i = 0; i < TI; ++i) cf[i] = cf[i] * sbw;
-      }
-    }
-    // one promotion FMA: acc[i][j][e] += P * (sA * sB)
-    auto fold = [&](int i, int j, int e, float p) {
-      if constexpr (GB == FP8Q_GRAN_128x128)
-        acc[i][j][e] = __builtin_fmaf(p, cf[i], acc[i][j][e]);
-      else
-        acc[i][j][e] = __builtin_fmaf(p * cf[i], sbv[j][e], acc[i][j][e]);
-    };
-    v4f pp[TJ], pn[TJ];
-    if constexpr (FAST) {
-      // 16x16x128: the lane holds logical chunks 2q, 2q+1 (q = l/16) of its row
-      const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
-      auto frag = [&](const uint8_t* base) {
-        const u32x4 x0 = *(const u32x4*)(base + o0);
-        const u32x4 x1 = *(const u32x4*)(base + o1);
-        return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      };
-      v8i fb[TJ];
-#pragma unroll
-      for (int j = 0; j < TJ; ++j) fb[j] = frag(lb + 16 * j * BK);
-      v8i fa = frag(la), fn = fa;
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        if (i + 1 < TI) fn = frag(la + 16 * (i + 1) * BK);
+        sbw = sb_blk[kb * sB_skb];
+      } else {
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, v4f{0.0f, 0.0f, 0.0f, 0.0f}, FB,
-                                                                  FA, 0, 0, 0, 0);
-          pin(pn[j]);
-          if (i > 0) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) fold(i - 1, j, e, pp[j][e]);
-            pin(acc[i - 1][j]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          const float4 t = *(const float4*)(lds_sb[s] + wn * TJ * 16 + 16 * j + 4 * lq);
+          sbv[j] = v4f{t.x, t.y, t.z, t.w};
         }
-#pragma unroll
-        for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
-        fa = fn;
       }
-    } else {
-      // 16x16x32 bf16, four per block.  Inside the block the K positions are
-      // assigned so that lane group q (= l/16) owns the contiguous bytes
-      // 32q .. 32q+32 of the block for all four MFMAs, bytes 8kk .. +8 of
-      // them going to MFMA kk; A and B use the same assignment, so every
-      // product still pairs matching k.  Each lane reads its 32 bytes with
-      // two 16-byte LDS reads, as on the FP8 path.
-      const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
-      auto raw32 = [&](const uint8_t* base, u32x2* r) {
-        const u32x4 x0 = *(const u32x4*)(base + o0);
-        const u32x4 x1 = *(const u32x4*)(base + o1);
-        r[0] = u32x2{x0.x, x0.y};
-        r[1] = u32x2{x0.z, x0.w};
-        r[2] = u32x2{x1.x, x1.y};
-        r[3] = u32x2{x1.z, x1.w};
-      };
-      constexpr bool H16 = H16X;
-      using V8 = typename Mf<H16>::v8;
-      using V2 = typename Mf<H16>::v2;
-      V8(&fb)[TJ][4] = xfb;
-      V8 fa[4];
+      const uint8_t* la = lds_a[s] + a_row0;
+      const uint8_t* lb = lds_b[s] + b_row0;
+      // the lane's TI A scales (times the block's B scale with 128x128 B scales)
+      float cf[TI];
+      {
+        const float* lc = lds_sa[s] + wm * TI * 16 + lr * TI;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) fa[kk] = xfa[kk];
-#pragma unroll
-      for (int i = 0; i < TI; ++i) {
-        u32x2 raw[4];
-        if (i + 1 < TI) raw32(la + 16 * (i + 1) * BK, raw);
-        // Before the last row tile: wait for block kb+1's copies (the newer
-        // block's may stay in flight), publish it with the barrier, and read
-        // its B fragments and first A fragment; they are decoded into the
-        // registers the last row tile's MFMAs release.  Every read of stage
-        // s precedes this barrier, which is what lets the copy of block kb+2
-        // (issued when block kb+1 starts) overwrite stage s's predecessor.
-        u32x2 rb[TJ][4], ra[4];
-        if constexpr (PF) {
-          if (i + 1 == TI) {
-            if (wait_all)
-              asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            else
-              asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NW) : "memory");
-            __syncthreads();
-            const uint8_t* lbn = lds_b[nxt] + b_row0;
-#pragma unroll
-            for (int j = 0; j < TJ; ++j) raw32(lbn + 16 * j * BK, rb[j]);
-            raw32(lds_a[nxt] + a_row0, ra);
-          }
+        for (int q = 0; q < TI / 4; ++q) {
+          const float4 c4 = *(const float4*)(lc + 4 * q);
+          cf[4 * q] = c4.x;
+          cf[4 * q + 1] = c4.y;
+          cf[4 * q + 2] = c4.z;
+          cf[4 * q + 3] = c4.w;
         }
-        V2 part[4][4];
+        if constexpr (GB == FP8Q_GRAN_128x128) {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+          for (int i = 0; i < TI; ++i) cf[i] = cf[i] * sbw;
+        }
+      }
+      // one promotion FMA: acc[i][j][e] += P * (sA * sB)
+      auto fold = [&](int i, int j, int e, float p) {
+        if constexpr (GB == FP8Q_GRAN_128x128)
+          acc[i][j][e] = __builtin_fmaf(p, cf[i], acc[i][j][e]);
+        else
+          acc[i][j][e] = __builtin_fmaf(p * cf[i], sbv[j][e], acc[i][j][e]);
+      };
+      v4f pp[TJ], pn[TJ];
+      if constexpr (FAST) {
+        // 16x16x128: the lane holds logical chunks 2q, 2q+1 (q = l/16) of its row
+        const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
+        auto frag = [&](const uint8_t* base) {
+          const u32x4 x0 = *(const u32x4*)(base + o0);
+          const u32x4 x1 = *(const u32x4*)(base + o1);
+          return v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+        };
+        v8i fb[TJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) fb[j] = frag(lb + 16 * j * BK);
+        v8i fa = frag(la), fn = fa;
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          if (i + 1 < TI) fn = frag(la + 16 * (i + 1) * BK);
 #pragma unroll
           for (int j = 0; j < TJ; ++j) {
-            pn[j] = mfma16x32<H16>(fb[j][kk], fa[kk], kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j]);
-            if (i > 0) fold(i - 1, j, kk, pp[j][kk]);
-            if (i + 1 < TI) {
-              // decode part j (two codes) of the next row tile's fragment kk
-              const uint32_t w = (j & 2) ? raw[kk].y : raw[kk].x;
-              part[kk][j] = (j & 1) ? dec2x<FA, H16, true>(w) : dec2x<FA, H16, false>(w);
-            } else if constexpr (PF) {
-              // the next block's fragments, into the registers just released
-              fb[j][kk] = dec8x<FB, H16>(rb[j][kk]);
-              if (j + 1 == TJ) xfa[kk] = dec8x<FA, H16>(ra[kk]);
-            }
-          }
-        if (i + 1 < TI) {
+            pn[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa, v4f{0.0f, 0.0f, 0.0f, 0.0f}, FB,
+                                                                    FA, 0, 0, 0, 0);
+            pin(pn[j]);
+            if (i > 0) {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            V8 f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              f[2 * q] = part[kk][q][0];
-              f[2 * q + 1] = part[kk][q][1];
+              for (int e = 0; e < 4; ++e) fold(i - 1, j, e, pp[j][e]);
+              pin(acc[i - 1][j]);
             }
-            fa[kk] = f;
+            __builtin_amdgcn_sched_barrier(0);
           }
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
+          fa = fn;
         }
+      } else {
+        // 16x16x32 bf16, four per block.  Inside the block the K positions are
+        // assigned so that lane group q (= l/16) owns the contiguous bytes
+        // 32q .. 32q+32 of the block for all four MFMAs, bytes 8kk .. +8 of
+        // them going to MFMA kk; A and B use the same assignment, so every
+        // product still pairs matching k.  Each lane reads its 32 bytes with
+        // two 16-byte LDS reads, as on the FP8 path.
+        const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
+        auto raw32 = [&](const uint8_t* base, u32x2* r) {
+          const u32x4 x0 = *(const u32x4*)(base + o0);
+          const u32x4 x1 = *(const u32x4*)(base + o1);
+          r[0] = u32x2{x0.x, x0.y};
+          r[1] = u32x2{x0.z, x0.w};
+          r[2] = u32x2{x1.x, x1.y};
+          r[3] = u32x2{x1.z, x1.w};
+        };
+        constexpr bool H16 = H16X;
+        using V8 = typename Mf<H16>::v8;
+        using V2 = typename Mf<H16>::v2;
+        V8(&fb)[TJ][4] = xfb;
+        V8 fa[4];
 #pragma unroll
-        for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
+        for (int kk = 0; kk < 4; ++kk) fa[kk] = xfa[kk];
+#pragma unroll
+        for (int i = 0; i < TI; ++i) {
+          u32x2 raw[4];
+          if (i + 1 < TI) raw32(la + 16 * (i + 1) * BK, raw);
+          // Before the last row tile: wait for block kb+1's copies (the newer
+          // block's may stay in flight), publish it with the barrier, and read
+          // its B fragments and first A fragment; they are decoded into the
+          // registers the last row tile's MFMAs release.  Every read of stage
+          // s precedes this barrier, which is what lets the copy of block kb+2
+          // (issued when block kb+1 starts) overwrite stage s's predecessor.
+          u32x2 rb[TJ][4], ra[4];
+          if constexpr (PF) {
+            if (i + 1 == TI) {
+              if (wait_all)
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+              else
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NW) : "memory");
+              __syncthreads();
+              const uint8_t* lbn = lds_b[nxt] + b_row0;
+#pragma unroll
+              for (int j = 0; j < TJ; ++j) raw32(lbn + 16 * j * BK, rb[j]);
+              raw32(lds_a[nxt] + a_row0, ra);
+            }
+          }
+          V2 part[4][4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j) {
+              pn[j] = mfma16x32<H16>(fb[j][kk], fa[kk], kk == 0 ? v4f{0.0f, 0.0f, 0.0f, 0.0f} : pn[j]);
+              if (i > 0) fold(i - 1, j, kk, pp[j][kk]);
+              if (i + 1 < TI) {
+                // decode part j (two codes) of the next row tile's fragment kk
+                const uint32_t w = (j & 2) ? raw[kk].y : raw[kk].x;
+                part[kk][j] = (j & 1) ? dec2x<FA, H16, true>(w) : dec2x<FA, H16, false>(w);
+              } else if constexpr (PF) {
+                // the next block's fragments, into the registers just released
+                fb[j][kk] = dec8x<FB, H16>(rb[j][kk]);
+                if (j + 1 == TJ) xfa[kk] = dec8x<FA, H16>(ra[kk]);
+              }
+            }
+          if (i + 1 < TI) {
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              V8 f;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                f[2 * q] = part[kk][q][0];
+                f[2 * q + 1] = part[kk][q][1];
+              }
+              fa[kk] = f;
+            }
+          }
+#pragma unroll
+          for (int j = 0; j < TJ; ++j) pp[j] = pn[j];
+        }
       }
-    }
-    // the last row tile's promotion
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) fold(TI - 1, j, e, pp[j][e]);
-  };
-
-  // Everything one wavefront copies into LDS stage st for K block kb.
-  // PAIRCOPY: wavefronts 0-3 copy their share and that of wavefront w+4
-  // (2*NL loads) and the others copy nothing; otherwise each copies its NL.
-  // Every wait allows NW loads in flight.
-  auto stage_block = [&](int64_t kb, int st) {
-    if constexpr (PAIRCOPY) {
-      if (wm != 0) return;
-      dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
-      dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
-      dma_tile<BM>(lds_a[st], A + kb * BK, a_off2, wave + 4);
-      dma_tile<BN>(lds_b[st], B + kb * BK, b_off2, wave + 4);
-      if (lane < SA_LANES) {
-        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
-        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + (wave + 4) * SA_LANES)),
-                 sa_row2 + kb * sA_skb);
-      }
-    } else {
-      dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
-      dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
-      if (lane < SA_LANES)
-        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
-      if (lane < SB_LANES)
-        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + wave * SB_LANES)), sb_col + kb * sB_skb);
-    }
-  };
-  auto next_stage = [](int st) { return st + 1 == NST ? 0 : st + 1; };
-
-  // Prologue: the first NST-1 blocks in flight, wait for block 0.
-  stage_block(0, 0);
-  if constexpr (NST == 3) {
-    if (nkb > 1) {
-      stage_block(1, 1);
-      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NW) : "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  __syncthreads();
-
-  using PF1 = std::integral_constant<bool, true>;
-  using PF0 = std::integral_constant<bool, false>;
-  int st = 0;
-  int64_t kb = 0;
-  if constexpr (FAST) {
-    // Steady state, no branches: copy block kb+1 while computing block kb,
-    // then wait for it and publish it with a barrier.
-    for (; kb + 1 < nkb; ++kb) {
-      stage_block(kb + 1, next_stage(st));
-      compute(kb, st, PF0{}, 0, true);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      st = next_stage(st);
-    }
-    compute(kb, st, PF0{}, 0, true);
-  } else {
-    // Block 0's first fragments, then the steady state: copy block kb+2
-    // while computing block kb, whose last row tile publishes block kb+1
-    // and decodes its first fragments.
-    {
-      const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
-      auto dec32 = [&](const uint8_t* base, auto fmt, typename Mf<H16X>::v8* out) {
-        const u32x4 x0 = *(const u32x4*)(base + o0);
-        const u32x4 x1 = *(const u32x4*)(base + o1);
-        constexpr int F = decltype(fmt)::value;
-        out[0] = dec8x<F, H16X>(u32x2{x0.x, x0.y});
-        out[1] = dec8x<F, H16X>(u32x2{x0.z, x0.w});
-        out[2] = dec8x<F, H16X>(u32x2{x1.x, x1.y});
-        out[3] = dec8x<F, H16X>(u32x2{x1.z, x1.w});
-      };
+      // the last row tile's promotion
 #pragma unroll
       for (int j = 0; j < TJ; ++j)
-        dec32(lds_b[0] + b_row0 + 16 * j * BK, std::integral_constant<int, FB>{}, xfb[j]);
-      dec32(lds_a[0] + a_row0, std::integral_constant<int, FA>{}, xfa);
-    }
-    for (; kb + 2 < nkb; ++kb) {
-      const int s1 = next_stage(st), s2 = next_stage(s1);
-      stage_block(kb + 2, s2);
-      compute(kb, st, PF1{}, s1, false);
-      st = s1;
-    }
-    if (kb + 1 < nkb) {
-      compute(kb, st, PF1{}, next_stage(st), true);
-      st = next_stage(st);
-      ++kb;
-    }
-    compute(kb, st, PF0{}, 0, true);
-  }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) fold(TI - 1, j, e, pp[j][e]);
+    };
 
-  // ---- epilogue.  Staging regions for C: TI*TJ*512 bytes per wavefront
-  // inside the K-loop stages.
-  constexpr int WB = TI * 16 * TJ * 16 * 2;
-  static_assert(FAST ? 4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b)
-                     : 8 * WB <= (int)sizeof(lds_b), "C staging does not fit");
-  uint8_t* stg = FAST ? (wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB)
-                      : &lds_b[0][0] + wave * WB;
-  if constexpr (ODT >= kOutQT) {
-    static_assert(!FAST, "the quantized outputs are on the exact path");
-    constexpr int QF = ODT & 1;
-    epilogue_qt<QF, TI, TJ>(acc, lds_cmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, N, qeps, Ct, ldt, Cst, ld_st,
-                            m0 / 128, wm == 0);
-    if constexpr (ODT >= kOutQB)
-      epilogue_q<QF, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps, (uint8_t*)C,
-                             ldc, Cs, ld_cs, (wn & 1) == 0);
-  } else if constexpr (ODT >= kOutQ) {
-    epilogue_q<ODT - kOutQ, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps,
-                                    (uint8_t*)C, ldc, Cs, ld_cs, (wn & 1) == 0);
-  } else {
-    store_c<ODT, TI, TJ>(acc, stg, lane, C, ldc, m0 + wm * TI * 16, wcol0, M, N);
+    // Everything one wavefront copies into LDS stage st for K block kb.
+    // PAIRCOPY: wavefronts 0-3 copy their share and that of wavefront w+4
+    // (2*NL loads) and the others copy nothing; otherwise each copies its NL.
+    // Every wait allows NW loads in flight.
+    auto stage_block = [&](int64_t kb, int st) {
+      if constexpr (PAIRCOPY) {
+        if (wm != 0) return;
+        dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+        dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
+        dma_tile<BM>(lds_a[st], A + kb * BK, a_off2, wave + 4);
+        dma_tile<BN>(lds_b[st], B + kb * BK, b_off2, wave + 4);
+        if (lane < SA_LANES) {
+          lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+          lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + (wave + 4) * SA_LANES)),
+                   sa_row2 + kb * sA_skb);
+        }
+      } else {
+        dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+        dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
+        if (lane < SA_LANES)
+          lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sa[st] + wave * SA_LANES)), sa_row + kb * sA_skb);
+        if (lane < SB_LANES)
+          lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_sb[st] + wave * SB_LANES)), sb_col + kb * sB_skb);
+      }
+    };
+    auto next_stage = [](int st) { return st + 1 == NST ? 0 : st + 1; };
+
+    // Prologue: the first NST-1 blocks in flight, wait for block 0.
+    stage_block(0, 0);
+    if constexpr (NST == 3) {
+      if (nkb > 1) {
+        stage_block(1, 1);
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NW) : "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+
+    using PF1 = std::integral_constant<bool, true>;
+    using PF0 = std::integral_constant<bool, false>;
+    int st = 0;
+    int64_t kb = 0;
+    if constexpr (FAST) {
+      // Steady state, no branches: copy block kb+1 while computing block kb,
+      // then wait for it and publish it with a barrier.
+      for (; kb + 1 < nkb; ++kb) {
+        stage_block(kb + 1, next_stage(st));
+        compute(kb, st, PF0{}, 0, true);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        st = next_stage(st);
+      }
+      compute(kb, st, PF0{}, 0, true);
+    } else {
+      // Block 0's first fragments, then the steady state: copy block kb+2
+      // while computing block kb, whose last row tile publishes block kb+1
+      // and decodes its first fragments.
+      {
+        const int o0 = 16 * swz_chunk<true>(lr, 2 * lq), o1 = 16 * swz_chunk<true>(lr, 2 * lq + 1);
+        auto dec32 = [&](const uint8_t* base, auto fmt, typename Mf<H16X>::v8* out) {
+          const u32x4 x0 = *(const u32x4*)(base + o0);
+          const u32x4 x1 = *(const u32x4*)(base + o1);
+          constexpr int F = decltype(fmt)::value;
+          out[0] = dec8x<F, H16X>(u32x2{x0.x, x0.y});
+          out[1] = dec8x<F, H16X>(u32x2{x0.z, x0.w});
+          out[2] = dec8x<F, H16X>(u32x2{x1.x, x1.y});
+          out[3] = dec8x<F, H16X>(u32x2{x1.z, x1.w});
+        };
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
+          dec32(lds_b[0] + b_row0 + 16 * j * BK, std::integral_constant<int, FB>{}, xfb[j]);
+        dec32(lds_a[0] + a_row0, std::integral_constant<int, FA>{}, xfa);
+      }
+      for (; kb + 2 < nkb; ++kb) {
+        const int s1 = next_stage(st), s2 = next_stage(s1);
+        stage_block(kb + 2, s2);
+        compute(kb, st, PF1{}, s1, false);
+        st = s1;
+      }
+      if (kb + 1 < nkb) {
+        compute(kb, st, PF1{}, next_stage(st), true);
+        st = next_stage(st);
+        ++kb;
+      }
+      compute(kb, st, PF0{}, 0, true);
+    }
+
+    // ---- epilogue.  Staging regions for C: TI*TJ*512 bytes per wavefront
+    // inside the K-loop stages.
+    constexpr int WB = TI * 16 * TJ * 16 * 2;
+    static_assert(FAST ? 4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b)
+                       : 8 * WB <= (int)sizeof(lds_b), "C staging does not fit");
+    uint8_t* stg = FAST ? (wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB)
+                        : &lds_b[0][0] + wave * WB;
+    if constexpr (ODT >= kOutQT) {
+      static_assert(!FAST, "the quantized outputs are on the exact path");
+      constexpr int QF = ODT & 1;
+      epilogue_qt<QF, TI, TJ>(acc, lds_cmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, N, qeps, Ct, ldt, Cst, ld_st,
+                              m0 / 128, wm == 0);
+      if constexpr (ODT >= kOutQB)
+        epilogue_q<QF, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps, (uint8_t*)C,
+                               ldc, Cs, ld_cs, (wn & 1) == 0);
+    } else if constexpr (ODT >= kOutQ) {
+      epilogue_q<ODT - kOutQ, TI, TJ>(acc, lds_rmax, stg, wave, lane, m0 + wm * TI * 16, wcol0, M, N, qeps,
+                                      (uint8_t*)C, ldc, Cs, ld_cs, (wn & 1) == 0);
+    } else {
+      store_c<ODT, TI, TJ>(acc, stg, lane, C, ldc, m0 + wm * TI * 16, wcol0, M, N);
+    }
+    __syncthreads();  // the epilogue's LDS reads precede the next tile's copies
   }
 }
 
@@ -869,142 +880,159 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_mx(
   __shared__ __attribute__((aligned(16))) uint8_t lds_sa[2][BM * 4];
   __shared__ __attribute__((aligned(16))) uint8_t lds_sb[2][BN * 4];
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 2, wn = wave & 3;
-  int64_t tm, tn;
-  tile_of(blockIdx.x, gridDim.x, ntm, ntn, tm, tn);
-  const int64_t m0 = tm * BM, n0 = tn * BN;
-  const int64_t nkb = K / BK;
+  // persistent grid, as k_gemm
+  const int64_t ntiles = ntm * ntn;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    int64_t tm, tn;
+    tile_of(tile, ntiles, ntm, ntn, tm, tn);
+    const int64_t m0 = tm * BM, n0 = tn * BN;
+    const int64_t nkb = K / BK;
 
-  uint32_t a_off[BM / 64], b_off[BN / 64];
-  dma_offsets<BM, false>(a_off, lda, m0, M, wave, lane);
-  dma_offsets<BN, false>(b_off, ldb, n0, N, wave, lane);
-  // scales: wavefronts 0-3 copy the 4 bytes (one dword) of A rows
-  // 64w + lane, wavefronts 4-7 those of B rows 64(w-4) + lane
-  const bool sc_a = wave < 4;
-  const int64_t sc_r = (sc_a ? m0 : n0) + 64 * (wave & 3) + lane;
-  const int64_t sc_lim = sc_a ? M : N;
-  const uint8_t* sc_row = sc_a ? sA + (sc_r < sc_lim ? sc_r : sc_lim - 1) * ld_sa
-                               : sB + (sc_r < sc_lim ? sc_r : sc_lim - 1) * ld_sb;
+    uint32_t a_off[BM / 64], b_off[BN / 64];
+    dma_offsets<BM, false>(a_off, lda, m0, M, wave, lane);
+    dma_offsets<BN, false>(b_off, ldb, n0, N, wave, lane);
+    // scales: wavefronts 0-3 copy the 4 bytes (one dword) of A rows
+    // 64w + lane, wavefronts 4-7 those of B rows 64(w-4) + lane
+    const bool sc_a = wave < 4;
+    const int64_t sc_r = (sc_a ? m0 : n0) + 64 * (wave & 3) + lane;
+    const int64_t sc_lim = sc_a ? M : N;
+    const uint8_t* sc_row = sc_a ? sA + (sc_r < sc_lim ? sc_r : sc_lim - 1) * ld_sa
+                                 : sB + (sc_r < sc_lim ? sc_r : sc_lim - 1) * ld_sb;
 
-  v4f acc[TI][TJ];
+    v4f acc[TI][TJ];
 #pragma unroll
-  for (int i = 0; i < TI; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j = 0; j < TJ; ++j) acc[i][j] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int lr = lane & 15, lq = lane >> 4;
-  const int a_row0 = wm * TI * 16 + lr, b_row0 = wn * TJ * 16 + lr;
-  const int o0 = 16 * swz_chunk<false>(lr, lq), o1 = 16 * swz_chunk<false>(lr, lq + 4);
+    const int lr = lane & 15, lq = lane >> 4;
+    const int a_row0 = wm * TI * 16 + lr, b_row0 = wn * TJ * 16 + lr;
+    const int o0 = 16 * swz_chunk<false>(lr, lq), o1 = 16 * swz_chunk<false>(lr, lq + 4);
 
-  auto stage_block = [&](int64_t kb, int st) {
-    dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
-    dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
-    uint8_t* dst = sc_a ? lds_sa[st] + 256 * (wave & 3) : lds_sb[st] + 256 * (wave & 3);
-    lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
-  };
-  // copy p (0-3 A, 4-7 B, 8 the scale bytes) of block kb into stage st
-  auto stage_part = [&](int64_t kb, int st, int p) {
-    if (p < 4) {
-      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_a[st] + (wave * 4 + p) * 1024)), A + kb * BK, a_off[p]);
-    } else if (p < 8) {
-      lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_b[st] + (wave * 4 + p - 4) * 1024)), B + kb * BK,
-                b_off[p - 4]);
-    } else {
+    auto stage_block = [&](int64_t kb, int st) {
+      dma_tile<BM>(lds_a[st], A + kb * BK, a_off, wave);
+      dma_tile<BN>(lds_b[st], B + kb * BK, b_off, wave);
       uint8_t* dst = sc_a ? lds_sa[st] + 256 * (wave & 3) : lds_sb[st] + 256 * (wave & 3);
       lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
-    }
-  };
+    };
+    // copy p (0-3 A, 4-7 B, 8 the scale bytes) of block kb into stage st
+    auto stage_part = [&](int64_t kb, int st, int p) {
+      if (p < 4) {
+        lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_a[st] + (wave * 4 + p) * 1024)), A + kb * BK, a_off[p]);
+      } else if (p < 8) {
+        lds_dma16(__builtin_amdgcn_readfirstlane(lds_addr_of(lds_b[st] + (wave * 4 + p - 4) * 1024)), B + kb * BK,
+                  b_off[p - 4]);
+      } else {
+        uint8_t* dst = sc_a ? lds_sa[st] + 256 * (wave & 3) : lds_sb[st] + 256 * (wave & 3);
+        lds_dma4(__builtin_amdgcn_readfirstlane(lds_addr_of(dst)), (const float*)(sc_row + 4 * kb));
+      }
+    };
 
-  // B fragments and scales of the block being computed; A fragments and
-  // scales of two row tiles (the one computed and the next), by parity.
-  // Per stage, a lane reads at fixed offsets from four bases.
-  v8i fb[TJ], fa[2];
-  int sbj[TJ], sai[2];
-  auto load_b = [&](int st, int j) {
-    const uint8_t* lb = &lds_b[0][0] + st * (BN * BK) + b_row0 * BK + 16 * j * BK;
-    const u32x4 x0 = *(const u32x4*)(lb + o0);
-    const u32x4 x1 = *(const u32x4*)(lb + o1);
-    fb[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    sbj[j] = (&lds_sb[0][0])[st * (BN * 4) + (b_row0 + 16 * j) * 4 + lq];
-  };
-  auto load_a = [&](int st, int i) {
-    const uint8_t* la = &lds_a[0][0] + st * (BM * BK) + a_row0 * BK + 16 * i * BK;
-    const u32x4 x0 = *(const u32x4*)(la + o0);
-    const u32x4 x1 = *(const u32x4*)(la + o1);
-    fa[i & 1] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-    sai[i & 1] = (&lds_sa[0][0])[st * (BM * 4) + (a_row0 + 16 * i) * 4 + lq];
-  };
-  auto mma = [&](int i, int j) {
-    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i & 1], acc[i][j], FB, FA, 0, sbj[j], 0,
-                                                                sai[i & 1]);
-  };
-  // row tiles 0 .. TI-2 of a block, each with the next row tile's A read
-  auto rows = [&](int st, int64_t kbn) {
+    // B fragments and scales of the block being computed; A fragments and
+    // scales of two row tiles (the one computed and the next), by parity.
+    // Per stage, a lane reads at fixed offsets from four bases.
+    v8i fb[TJ], fa[2];
+    int sbj[TJ], sai[2];
+    auto load_b = [&](int st, int j) {
+      const uint8_t* lb = &lds_b[0][0] + st * (BN * BK) + b_row0 * BK + 16 * j * BK;
+      const u32x4 x0 = *(const u32x4*)(lb + o0);
+      const u32x4 x1 = *(const u32x4*)(lb + o1);
+      fb[j] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      sbj[j] = (&lds_sb[0][0])[st * (BN * 4) + (b_row0 + 16 * j) * 4 + lq];
+    };
+    auto load_a = [&](int st, int i) {
+      const uint8_t* la = &lds_a[0][0] + st * (BM * BK) + a_row0 * BK + 16 * i * BK;
+      const u32x4 x0 = *(const u32x4*)(la + o0);
+      const u32x4 x1 = *(const u32x4*)(la + o1);
+      fa[i & 1] = v8i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w, (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+      sai[i & 1] = (&lds_sa[0][0])[st * (BM * 4) + (a_row0 + 16 * i) * 4 + lq];
+    };
+    auto mma = [&](int i, int j) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fb[j], fa[i & 1], acc[i][j], FB, FA, 0, sbj[j], 0,
+                                                                  sai[i & 1]);
+    };
+    // row tiles 0 .. TI-2 of a block, each with the next row tile's A read
+    auto rows = [&](int st, int64_t kbn) {
 #pragma unroll
-    for (int i = 0; i + 1 < TI; ++i) {
-      load_a(st, i + 1);
+      for (int i = 0; i + 1 < TI; ++i) {
+        load_a(st, i + 1);
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          mma(i, j);
+          if (j == 0 && i < 5) stage_part(kbn, st ^ 1, 4 + i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    static_assert(TI % 2 == 0, "row tile 0 of every block uses A slot 0");
+
+    // Software pipeline over K blocks (two LDS stages, block kb in stage
+    // kb % 2).  The barrier that publishes block kb sits before the last row
+    // tile of block kb-1; after it the nine copies of block kb+1 go into the
+    // stage block kb-1 has finished with, one after each of the last row
+    // tile's MFMAs and one per row tile after that (a copy stalls the
+    // wavefront that issues it; spread out, the stalls fall between MFMAs
+    // instead of all at the block start), and the fragments of block kb are
+    // read behind the last row tile's MFMAs, so no block starts by waiting
+    // for its first LDS reads.  One pass of the loop is the last row tile of
+    // block kb-1 followed by the other row tiles of block kb.  The copies
+    // carry no condition: the last pass copies block nkb-1 once more, into
+    // the stage nothing reads any more.
+    stage_block(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    {
+      // block 1 (block 0 again when there is one block: stage 1 is then never read)
+      const int64_t k1 = nkb > 1 ? 1 : 0;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) stage_part(k1, 1, p);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) load_b(0, j);
+      load_a(0, 0);
+      rows(0, k1);
+    }
+    for (int64_t kb = 1; kb < nkb; ++kb) {
+      const int st = (int)(kb & 1);
+      // every lane's reads of stage st^1 are done and block kb has landed
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __syncthreads();
+      const int64_t kbn = kb + 1 < nkb ? kb + 1 : nkb - 1;
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
-        mma(i, j);
-        if (j == 0 && i < 5) stage_part(kbn, st ^ 1, 4 + i);
+        mma(TI - 1, j);
+        stage_part(kbn, st ^ 1, j);
+        load_b(st, j);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
+      load_a(st, 0);
+      rows(st, kbn);
     }
-  };
-  static_assert(TI % 2 == 0, "row tile 0 of every block uses A slot 0");
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) mma(TI - 1, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // Software pipeline over K blocks (two LDS stages, block kb in stage
-  // kb % 2).  The barrier that publishes block kb sits before the last row
-  // tile of block kb-1; after it the nine copies of block kb+1 go into the
-  // stage block kb-1 has finished with, one after each of the last row
-  // tile's MFMAs and one per row tile after that (a copy stalls the
-  // wavefront that issues it; spread out, the stalls fall between MFMAs
-  // instead of all at the block start), and the fragments of block kb are
-  // read behind the last row tile's MFMAs, so no block starts by waiting
-  // for its first LDS reads.  One pass of the loop is the last row tile of
-  // block kb-1 followed by the other row tiles of block kb.  The copies
-  // carry no condition: the last pass copies block nkb-1 once more, into
-  // the stage nothing reads any more.
-  stage_block(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  {
-    // block 1 (block 0 again when there is one block: stage 1 is then never read)
-    const int64_t k1 = nkb > 1 ? 1 : 0;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) stage_part(k1, 1, p);
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) load_b(0, j);
-    load_a(0, 0);
-    rows(0, k1);
+    // ---- epilogue
+    constexpr int WB = TI * 16 * TJ * 16 * 2;
+    static_assert(4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b), "C staging does not fit");
+    uint8_t* stg = wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB;
+    store_c<ODT, TI, TJ>(acc, stg, lane, C, ldc, m0 + wm * TI * 16, n0 + wn * TJ * 16, M, N);
+    __syncthreads();  // the epilogue's LDS reads precede the next tile's copies
   }
-  for (int64_t kb = 1; kb < nkb; ++kb) {
-    const int st = (int)(kb & 1);
-    // every lane's reads of stage st^1 are done and block kb has landed
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    __syncthreads();
-    const int64_t kbn = kb + 1 < nkb ? kb + 1 : nkb - 1;
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      mma(TI - 1, j);
-      stage_part(kbn, st ^ 1, j);
-      load_b(st, j);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    load_a(st, 0);
-    rows(st, kbn);
-  }
-#pragma unroll
-  for (int j = 0; j < TJ; ++j) mma(TI - 1, j);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
-  // ---- epilogue
-  constexpr int WB = TI * 16 * TJ * 16 * 2;
-  static_assert(4 * WB <= (int)sizeof(lds_a) && 4 * WB <= (int)sizeof(lds_b), "C staging does not fit");
-  uint8_t* stg = wave < 4 ? &lds_a[0][0] + wave * WB : &lds_b[0][0] + (wave - 4) * WB;
-  store_c<ODT, TI, TJ>(acc, stg, lane, C, ldc, m0 + wm * TI * 16, n0 + wn * TJ * 16, M, N);
+// Workgroups of a GEMM launch: one per compute unit, rounded down to a
+// multiple of 8 so that workgroup b and its tiles b + grid, b + 2 grid, ...
+// stay on XCD b % 8 (the tile order below keeps each XCD's tiles together),
+// or one per tile when there are fewer tiles.
+static int64_t persistent_grid(int64_t tiles) {
+  int64_t g = (device_cu_count() / 8) * 8;
+  if (g < 8) g = 8;
+  return tiles < g ? tiles : g;
 }
 
 template <int FA, int FB, int ODT>
@@ -1012,8 +1040,8 @@ static void launch_mx_t(const uint8_t* A, int64_t lda, const uint8_t* sA, int64_
                         int64_t ldb, const uint8_t* sB, int64_t ld_sb, void* C, int64_t ldc, int64_t M, int64_t N,
                         int64_t K, hipStream_t st) {
   const int64_t ntm = (M + 255) / 256, ntn = (N + 255) / 256;
-  hipLaunchKernelGGL((k_gemm_mx<FA, FB, ODT>), dim3((unsigned)(ntm * ntn)), dim3(kGemmThreads), 0, st, A, lda, sA,
-                     ld_sa, B, ldb, sB, ld_sb, C, ldc, M, N, K, ntm, ntn);
+  hipLaunchKernelGGL((k_gemm_mx<FA, FB, ODT>), dim3((unsigned)persistent_grid(ntm * ntn)), dim3(kGemmThreads), 0, st,
+                     A, lda, sA, ld_sa, B, ldb, sB, ld_sb, C, ldc, M, N, K, ntm, ntn);
 }
 
 int launch_gemm_mx(const uint8_t* A, int fa, int64_t lda, const uint8_t* sA, int64_t ld_sa, const uint8_t* B,
@@ -1056,9 +1084,9 @@ static void launch_t(const uint8_t* A, int64_t lda, const float* sA, int64_t sA_
                      int64_t ld_cs = 0, float qeps = 0.0f, QtOut qt = QtOut{}) {
   constexpr int BM = Cfg<FAST>::BM, BN = Cfg<FAST>::BN;
   const int64_t ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((k_gemm<FA, FB, GB, ODT, FAST>), dim3((unsigned)(ntm * ntn)), dim3(kGemmThreads), 0, st, A,
-                     lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, Cs, ld_cs, qeps, qt.Ct, qt.ldt,
-                     qt.Cst, qt.ld_st, M, N, K, ntm, ntn);
+  hipLaunchKernelGGL((k_gemm<FA, FB, GB, ODT, FAST>), dim3((unsigned)persistent_grid(ntm * ntn)), dim3(kGemmThreads),
+                     0, st, A, lda, sA, sA_sm, sA_skb, B, ldb, sB, sB_sn, sB_skb, C, ldc, Cs, ld_cs, qeps, qt.Ct,
+                     qt.ldt, qt.Cst, qt.ld_st, M, N, K, ntm, ntn);
 }
 
 template <int FA, int FB, int GB>
