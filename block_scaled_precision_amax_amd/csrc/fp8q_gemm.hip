@@ -47,6 +47,7 @@ namespace fp8q {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -432,7 +433,9 @@ __device__ __forceinline__ void store_staged(const v4f (&acc)[TI][TJ], T* stg, i
       const int col = 16 * j + 4 * lq;
       T* d = stg + r * W + EPC * ((col / EPC) ^ sw(r)) + col % EPC;
       if constexpr (ES == 2)
-        *(u32x2*)d = u32x2{f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16), f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+        // v_cvt_pk_bf16_f32: round to nearest even, subnormals kept
+        *(u32x2*)d = u32x2{__builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{v[0], v[1]}, v2bf)),
+                           __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{v[2], v[3]}, v2bf))};
       else
         *(v4f*)d = v;
     }

@@ -91,13 +91,6 @@ FP8Q_DEV bool scale_ok(float s) { return s >= 0x1p-80f && s <= 0x1p80f; }
 FP8Q_DEV float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
 FP8Q_DEV float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, round to nearest even, NaN -> 0x7FC0.
-FP8Q_DEV uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f != f) return 0x7FC0u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // Scale from a block amax: s = fl32(max(amax, eps) / MAX).  A NaN amax
 // gives a NaN scale (the comparison is false), as torch's clamp does.
 template <int FMT>
