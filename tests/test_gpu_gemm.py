@@ -231,6 +231,27 @@ def run_gemm_fast(fq, A, fa, sA, B, fb, sB, gb, out=torch.float32, dev="cuda"):
     return C.cpu()
 
 
+@pytest.mark.parametrize("fa,fb,gb", [(E4, E4, G128), (E5, E4, G1)])
+def test_gemm_persistent_uneven_tiles(fq, orc, gpu, fa, fb, gb):
+    """More tiles than the persistent grid has workgroups, in a count that is
+    neither a multiple of the grid nor of 8: workgroups walk different numbers
+    of tiles, in the order without the per-XCD renumbering.  Ragged M and N;
+    the exact path has 46 x 13 = 598 tiles of 128x256, the FP8-MFMA path 23 x
+    13 = 299 of 256x256.  Every element is checked, for both paths."""
+    M, N, K = 256 * 23 - 37, 256 * 13 - 100, 256
+    A = W.fp8_codes((M, K), fa, seed=71)
+    B = W.fp8_codes((N, K), fb, seed=72)
+    sA = rand_scales((M, K // 128), 73)
+    sB = rand_scales((((N + 127) // 128) if gb == G128 else N, K // 128), 74)
+    Cref, D = orc.gemm_blockscaled(A.numpy(), fa, sA.numpy(), B.numpy(), fb, sB.numpy(), gb)
+    C = run_gemm(fq, A, fa, sA, B, fb, sB, gb)
+    check(C, Cref, D, "exact path, uneven tiles")
+    Cb = run_gemm(fq, A, fa, sA, B, fb, sB, gb, out=torch.bfloat16)
+    assert torch.equal(Cb.view(torch.int16), bf16_of(C).view(torch.int16))
+    Cf = run_gemm_fast(fq, A, fa, sA, B, fb, sB, gb).to(torch.float64).numpy()
+    assert np.all(np.abs(Cf - Cref) <= FAST_TOL * D)
+
+
 @pytest.mark.parametrize("fa,fb,gb", [(E4, E4, G128), (E5, E4, G128), (E5, E4, G1), (E4, E5, G1)])
 @pytest.mark.parametrize("M,N,K", [(200, 384, 512), (300, 200, 384), (5, 1, 128), (33, 130, 256)])
 def test_gemm_fast_random_codes(fq, orc, gpu, fa, fb, gb, M, N, K):

@@ -203,6 +203,20 @@ def test_gemm_mx_random_codes(fq, orc, gpu, fa, fb, M, N, K):
     assert torch.equal(Cb.view(torch.int16), C.to(torch.bfloat16).view(torch.int16))
 
 
+def test_gemm_mx_persistent_uneven_tiles(fq, orc, gpu):
+    """23 x 13 = 299 tiles of 256x256 with ragged M and N: more than the
+    persistent grid's workgroups and a multiple of neither it nor 8, so the
+    workgroups walk different numbers of tiles.  Every element is checked."""
+    M, N, K = 256 * 23 - 37, 256 * 13 - 100, 256
+    A = W.fp8_codes((M, K), E4, seed=81)
+    B = W.fp8_codes((N, K), E4, seed=82)
+    sA = rand_e8m0((M, K // 32), 83)
+    sB = rand_e8m0((N, K // 32), 84)
+    C = run_gemm_mx(fq, A, E4, sA, B, E4, sB)
+    Cref, D = orc.gemm_mx(A.numpy(), E4, sA.numpy(), B.numpy(), E4, sB.numpy())
+    check_mx(C, Cref, D, "uneven tiles")
+
+
 def test_gemm_mx_strided(fq, orc, gpu):
     M, N, K = 130, 300, 640
     A = W.fp8_codes((M, K), E4, seed=5)
