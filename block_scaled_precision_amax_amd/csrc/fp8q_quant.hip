@@ -413,11 +413,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict
 // walks FP8Q_RT consecutive 128-row blocks of it, loading the next block
 // while it encodes the current one; each load instruction reads 256-byte
 // (bf16, W = 128) pieces of four rows.  Each 128xW tile is staged in LDS in
-// its input type with the column index XORed by 16*((row/16) mod 4), which
-// keeps the row-wise staging writes and the column-wise reads free of bank
-// conflicts.  The four lanes of a quad hold one column's 128 values, reduce
-// its amax with two shuffles and write its 128 codes as one contiguous run
-// of the transposed output.
+// its input type, swizzled so that the row-wise staging writes and the
+// column-wise reads are free of bank conflicts.  bf16: eight lanes hold a
+// pair of columns' 128 values (one dword per row), reduce both amaxes with
+// packed 16-bit maxima and three shuffles, and write each column's 128
+// codes as one contiguous run of the transposed output; fp32: the four
+// lanes of a quad do the same for one column.
 #ifndef FP8Q_RT
 #define FP8Q_RT 8  // row blocks per workgroup in the transposed quantizer (measured)
 #endif
@@ -449,13 +450,17 @@ __global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict_
       v[i] = __builtin_nontemporal_load((const u32x4*)(xb + ((rb * 128 + t) * ldx + c0 + c) * esz));
     }
   };
-  // thread (f, k): column f, rows 16k .. 16k+16 and 64+16k .. 64+16k+16,
-  // so that each of its two 16-byte code stores lands next to those of the
-  // other three lanes of the quad (64 contiguous bytes per store)
-  auto swz = [](int t) { return 16 * ((t >> 4) & 3); };
-  const int f = tid >> 2, k = tid & 3;
-  const int fc = f ^ (16 * k);
-  const int64_t col = c0 + f;
+  // fp32: thread (f, k) takes column f, rows 16k .. 16k+16 and 64+16k ..
+  // 64+16k+16, so that each of its two 16-byte code stores lands next to
+  // those of the other three lanes of the quad (64 contiguous bytes per
+  // store).  bf16: thread (p, k) takes the column pair p (columns 2p, 2p+1,
+  // one dword of the tile row) over rows 16k .. 16k+16, so one 4-byte LDS
+  // read brings two columns and their amax is one packed 16-bit max; the
+  // eight lanes k = 0..7 of a pair write 128 contiguous code bytes per
+  // column.  Staging swizzles: fp32 XORs the column by 16*((t/16) mod 4),
+  // bf16 XORs the column pair by 8*((t/16) mod W/16); both keep the row-wise
+  // 16-byte writes whole and the column-wise reads free of bank conflicts.
+  auto swz = [](int t) { return DT == FP8Q_F32 ? 16 * ((t >> 4) & 3) : 16 * ((t >> 4) & (W / 16 - 1)); };
   // One row block: stage the tile, reduce each column's amax, encode, store.
   auto block = [&](int64_t rb, const u32x4* v) {
 #pragma unroll
@@ -467,37 +472,78 @@ __global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict_
         *(u32x4*)(tile16 + t * W + (c ^ swz(t))) = v[i];
     }
     __syncthreads();
-    float a[32];
-    uint32_t m = 0;
+    if constexpr (DT == FP8Q_F32) {
+      const int f = tid >> 2, k = tid & 3;
+      const int fc = f ^ (16 * k);
+      const int64_t col = c0 + f;
+      float a[32];
+      uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int t = 16 * k + (j & 15) + 64 * (j >> 4);  // swz(t) == 16k
-      if constexpr (DT == FP8Q_F32)
+      for (int j = 0; j < 32; ++j) {
+        const int t = 16 * k + (j & 15) + 64 * (j >> 4);  // swz(t) == 16k
         a[j] = tile[t * W + fc];
-      else
-        a[j] = __uint_as_float((uint32_t)tile16[t * W + fc] << 16);
-      m = max(m, __float_as_uint(a[j]) & 0x7FFFFFFFu);
-    }
-    __syncthreads();  // the tile is rewritten by the next row block
-    m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-    m = max(m, (uint32_t)__shfl_xor((int)m, 2));
-    const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
-    if (k == 0) scales[col * ld_s + rb] = s;
-    uint32_t w[8];
-    if (scale_ok(s)) {
-      // |x| <= amax, so x/s stays within the finite range
-      const float r = 1.0f / s;
+        m = max(m, __float_as_uint(a[j]) & 0x7FFFFFFFu);
+      }
+      __syncthreads();  // the tile is rewritten by the next row block
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+      const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
+      if (k == 0) scales[col * ld_s + rb] = s;
+      uint32_t w[8];
+      if (scale_ok(s)) {
+        // |x| <= amax, so x/s stays within the finite range
+        const float r = 1.0f / s;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = pack4<FMT>(sat<FMT>(div_rn(a[4 * i], s, r)), sat<FMT>(div_rn(a[4 * i + 1], s, r)),
-                          sat<FMT>(div_rn(a[4 * i + 2], s, r)), sat<FMT>(div_rn(a[4 * i + 3], s, r)));
+        for (int i = 0; i < 8; ++i)
+          w[i] = pack4<FMT>(sat<FMT>(div_rn(a[4 * i], s, r)), sat<FMT>(div_rn(a[4 * i + 1], s, r)),
+                            sat<FMT>(div_rn(a[4 * i + 2], s, r)), sat<FMT>(div_rn(a[4 * i + 3], s, r)));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = quant4_exact<FMT>(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3], s);
+      }
+      uint8_t* qrow = q + col * ldq + rb * 128 + 16 * k;
+      __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)qrow);
+      __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, (u32x4*)(qrow + 64));
     } else {
+      const int p = tid >> 3, k = tid & 7;
+      const int pc = p ^ (8 * (k & (W / 16 - 1)));  // the pair's slot in rows 16k .. 16k+16
+      const uint32_t* trow = tile_raw + (16 * k) * (W / 2) + pc;
+      uint32_t d[16];
+      uint32_t m = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = quant4_exact<FMT>(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3], s);
+      for (int j = 0; j < 16; ++j) {
+        d[j] = trow[j * (W / 2)];
+        m = pk_absmax(m, d[j]);
+      }
+      __syncthreads();  // the tile is rewritten by the next row block
+      // amax of each column over the eight lanes of the pair
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        const uint32_t mo = (uint32_t)__shfl_xor((int)m, o);
+        m = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, m),
+                                                                   __builtin_bit_cast(u16x2, mo)));
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t col = c0 + 2 * p + h;
+        const uint32_t mb = h ? (m & 0xFFFF0000u) : (m << 16);
+        const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(mb)), eps);
+        if (k == 0) scales[col * ld_s + rb] = s;
+        auto val = [&](int j) { return h ? bf_hi(d[j]) : bf_lo(d[j]); };
+        uint32_t w[4];
+        if (scale_ok(s)) {
+          const float r = 1.0f / s;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            w[i] = pack4<FMT>(sat<FMT>(div_rn(val(4 * i), s, r)), sat<FMT>(div_rn(val(4 * i + 1), s, r)),
+                              sat<FMT>(div_rn(val(4 * i + 2), s, r)), sat<FMT>(div_rn(val(4 * i + 3), s, r)));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = quant4_exact<FMT>(val(4 * i), val(4 * i + 1), val(4 * i + 2), val(4 * i + 3), s);
+        }
+        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)(q + col * ldq + rb * 128 + 16 * k));
+      }
     }
-    uint8_t* qrow = q + col * ldq + rb * 128 + 16 * k;
-    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)qrow);
-    __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, (u32x4*)(qrow + 64));
   };
   // The next block's loads are issued unconditionally before the current
   // block is used (the last block is peeled off), so the wait before the
