@@ -103,6 +103,23 @@ def test_gemm_strided_operands(fq, orc, gpu):
             assert torch.all(Cb[:, N:] == -7.0), (ldc, fast)
 
 
+def test_gemm_bf16_output_subnormal(fq, orc, gpu):
+    """bf16 C is the round-to-nearest-even of the kernel's own fp32 C, bit for
+    bit, also where C lies in fp32's subnormal range (tiny scales; the
+    rounding keeps subnormals)."""
+    M, N, K = 64, 256, 256
+    A = W.fp8_codes((M, K), E4, seed=91)
+    B = W.fp8_codes((N, K), E4, seed=92)
+    sA = torch.full((M, K // 128), 2.0 ** -70, dtype=torch.float32)
+    sB = torch.full((N // 128, K // 128), 2.0 ** -70, dtype=torch.float32)
+    for fast in (False, True):
+        C32 = (run_gemm_fast if fast else run_gemm)(fq, A, E4, sA, B, E4, sB, G128)
+        Cb = (run_gemm_fast if fast else run_gemm)(fq, A, E4, sA, B, E4, sB, G128, out=torch.bfloat16)
+        c = C32.abs()
+        assert int(((c > 0) & (c < 2.0 ** -126)).sum()) > 100, "no subnormal outputs"
+        assert torch.equal(Cb.view(torch.int16), C32.to(torch.bfloat16).view(torch.int16)), fast
+
+
 def test_gemm_special_codes_non_finite(fq, orc, gpu):
     M, N, K = 64, 128, 256
     A = W.fp8_codes((M, K), E4, seed=9)
