@@ -86,20 +86,29 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 #ifndef FP8Q_G_T
 #define FP8Q_G_T 8
 #endif
+#ifndef FP8Q_G_TDQ
+#define FP8Q_G_TDQ 32  // the per-tensor quantizer writing the round trip as well
+#endif
 #ifndef FP8Q_TH_T
 #define FP8Q_TH_T 256  // threads per workgroup of the per-tensor quantizer
 #endif
 #ifndef FP8Q_G_MX
-#define FP8Q_G_MX 16
+#define FP8Q_G_MX 32
+#endif
+#ifndef FP8Q_KU_MX
+#define FP8Q_KU_MX 4
 #endif
 #ifndef FP8Q_G_1
-#define FP8Q_G_1 8
+#define FP8Q_G_1 32
 #endif
 #ifndef FP8Q_KU_D
 #define FP8Q_KU_D 4
 #endif
 #ifndef FP8Q_G_D
 #define FP8Q_G_D 32
+#endif
+#ifndef FP8Q_G_DMX
+#define FP8Q_G_DMX 128
 #endif
 
 template <int DT>
@@ -295,7 +304,7 @@ __global__ __launch_bounds__(FP8Q_TH_T) void k_quant_tensor(const void* __restri
 // wavefronts cover consecutive stretches, so each workgroup streams one
 // contiguous chunk of the (row, block) sequence at a time.
 #ifndef FP8Q_KGROUPS
-#define FP8Q_KGROUPS 4
+#define FP8Q_KGROUPS 2
 #endif
 static constexpr int kGroups = FP8Q_KGROUPS;
 
@@ -818,10 +827,10 @@ __global__ __launch_bounds__(kThreads) void k_dequant(const uint8_t* __restrict_
 // [-127, 127]), stored as the E8M0 byte e + 127; a block holding a NaN or an
 // Inf gets the NaN scale 0xFF and NaN codes; an all-zero block e = -127.
 // Codes are enc(x * 2^-e), a multiplication by a normal power of two, exact
-// wherever the code can be nonzero.  Each lane holds one 16-byte vector (8
-// bf16 or 4 fp32); the lanes of a block are consecutive (4 or 8) and reduce
-// the block maximum with xor shuffles.  Each workgroup walks a contiguous
-// chunk of vectors.
+// wherever the code can be nonzero.  A lane's 16-byte vector holds 8 bf16
+// or 4 fp32; the lanes of a block are consecutive (4 or 8) and reduce the
+// block maximum with xor shuffles.  Each workgroup walks a contiguous chunk
+// of vectors.
 template <int FMT>
 __device__ __forceinline__ int mx_exponent(uint32_t amax_bits) {
   constexpr int kEmax = FMT == FP8Q_E4M3FN ? 8 : 15;
@@ -843,43 +852,63 @@ __global__ __launch_bounds__(kThreads) void k_quant_mx(const void* __restrict__ 
   const char* xb = (const char*)x;
   const int64_t v0 = (int64_t)blockIdx.x * per_wg;
   const int64_t v1 = v0 + per_wg < nvec ? v0 + per_wg : nvec;
-  for (int64_t base = v0; base < v1; base += kThreads) {
-    // vectors are counted along rows; blocks never straddle a row (cols % 32 == 0)
-    // and per_wg is a multiple of the block's lane count, so a block's lanes
-    // are always active together
-    const int64_t v = base + threadIdx.x;
-    const bool on = v < v1;
-    const int64_t r = on ? v / vpr : 0, c = on ? (v - r * vpr) * VE : 0;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (on) w = __builtin_nontemporal_load((const u32x4*)(xb + (r * ldx + c) * esz));
-    uint32_t m;
-    if constexpr (DT == FP8Q_F32)
-      m = max(max(w.x & 0x7FFFFFFFu, w.y & 0x7FFFFFFFu), max(w.z & 0x7FFFFFFFu, w.w & 0x7FFFFFFFu));
-    else
-      m = pk_fold(pk_absmax(pk_absmax(pk_absmax(pk_absmax(0u, w.x), w.y), w.z), w.w));
+  // Each lane takes FP8Q_KU_MX vectors per pass (all loads first, kThreads
+  // vectors apart).  Vectors are counted along rows and blocks never
+  // straddle a row (cols % 32 == 0); per_wg is a multiple of kThreads and a
+  // row a multiple of the block's lane count, so a block's lanes are always
+  // active together.  The lane's (row, column) is divided out once and then
+  // stepped.
+  constexpr int U = FP8Q_KU_MX;
+  const int64_t cols = vpr * VE;
+  int64_t rn = (v0 + threadIdx.x) / vpr, cn = (v0 + threadIdx.x - rn * vpr) * VE;
+  for (int64_t base = v0; base < v1; base += (int64_t)U * kThreads) {
+    u32x4 w[U];
+    bool on[U];
+    int64_t r[U], c[U];
 #pragma unroll
-    for (int o = 1; o < LPB; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
-    if (!on) continue;
-    uint8_t* qp = q + r * ldq + c;
-    const bool special = m >= 0x7F800000u;  // a NaN or an Inf in the block
-    if ((threadIdx.x & (LPB - 1)) == 0) scales[r * ld_s + (c >> 5)] = special ? 0xFF : (uint8_t)(mx_exponent<FMT>(m) + 127);
-    if (special) {
-      if constexpr (DT == FP8Q_F32) *(uint32_t*)qp = 0x7F7F7F7Fu;
-      else *(u32x2*)qp = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
-      continue;
+    for (int u = 0; u < U; ++u) {
+      on[u] = base + u * kThreads + threadIdx.x < v1;
+      r[u] = rn;
+      c[u] = cn;
+      cn += kThreads * VE;
+      while (cn >= cols) {
+        cn -= cols;
+        ++rn;
+      }
+      w[u] = on[u] ? __builtin_nontemporal_load((const u32x4*)(xb + (r[u] * ldx + c[u]) * esz)) : u32x4{0u, 0u, 0u, 0u};
     }
-    const float inv = __uint_as_float((uint32_t)(127 - mx_exponent<FMT>(m)) << 23);  // 2^-e, normal
-    if constexpr (DT == FP8Q_F32) {
-      const uint32_t o = pack4<FMT>(sat<FMT>(__uint_as_float(w.x) * inv), sat<FMT>(__uint_as_float(w.y) * inv),
-                                    sat<FMT>(__uint_as_float(w.z) * inv), sat<FMT>(__uint_as_float(w.w) * inv));
-      __builtin_nontemporal_store(o, (uint32_t*)qp);
-    } else {
-      u32x2 o;
-      o.x = pack4<FMT>(sat<FMT>(bf_lo(w.x) * inv), sat<FMT>(bf_hi(w.x) * inv), sat<FMT>(bf_lo(w.y) * inv),
-                       sat<FMT>(bf_hi(w.y) * inv));
-      o.y = pack4<FMT>(sat<FMT>(bf_lo(w.z) * inv), sat<FMT>(bf_hi(w.z) * inv), sat<FMT>(bf_lo(w.w) * inv),
-                       sat<FMT>(bf_hi(w.w) * inv));
-      __builtin_nontemporal_store(o, (u32x2*)qp);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t m;
+      if constexpr (DT == FP8Q_F32)
+        m = max(max(w[u].x & 0x7FFFFFFFu, w[u].y & 0x7FFFFFFFu), max(w[u].z & 0x7FFFFFFFu, w[u].w & 0x7FFFFFFFu));
+      else
+        m = pk_fold(pk_absmax(pk_absmax(pk_absmax(pk_absmax(0u, w[u].x), w[u].y), w[u].z), w[u].w));
+#pragma unroll
+      for (int o = 1; o < LPB; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+      if (!on[u]) continue;
+      uint8_t* qp = q + r[u] * ldq + c[u];
+      const bool special = m >= 0x7F800000u;  // a NaN or an Inf in the block
+      if ((threadIdx.x & (LPB - 1)) == 0)
+        scales[r[u] * ld_s + (c[u] >> 5)] = special ? 0xFF : (uint8_t)(mx_exponent<FMT>(m) + 127);
+      if (special) {
+        if constexpr (DT == FP8Q_F32) *(uint32_t*)qp = 0x7F7F7F7Fu;
+        else *(u32x2*)qp = u32x2{0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        continue;
+      }
+      const float inv = __uint_as_float((uint32_t)(127 - mx_exponent<FMT>(m)) << 23);  // 2^-e, normal
+      if constexpr (DT == FP8Q_F32) {
+        const uint32_t o = pack4<FMT>(sat<FMT>(__uint_as_float(w[u].x) * inv), sat<FMT>(__uint_as_float(w[u].y) * inv),
+                                      sat<FMT>(__uint_as_float(w[u].z) * inv), sat<FMT>(__uint_as_float(w[u].w) * inv));
+        __builtin_nontemporal_store(o, (uint32_t*)qp);
+      } else {
+        u32x2 o;
+        o.x = pack4<FMT>(sat<FMT>(bf_lo(w[u].x) * inv), sat<FMT>(bf_hi(w[u].x) * inv), sat<FMT>(bf_lo(w[u].y) * inv),
+                         sat<FMT>(bf_hi(w[u].y) * inv));
+        o.y = pack4<FMT>(sat<FMT>(bf_lo(w[u].z) * inv), sat<FMT>(bf_hi(w[u].z) * inv), sat<FMT>(bf_lo(w[u].w) * inv),
+                         sat<FMT>(bf_hi(w[u].w) * inv));
+        __builtin_nontemporal_store(o, (u32x2*)qp);
+      }
     }
   }
 }
@@ -895,12 +924,13 @@ __global__ __launch_bounds__(kThreads) void k_dequant_mx(const uint8_t* __restri
   const int64_t total = rows * gpr;
   const int64_t g0 = (int64_t)blockIdx.x * per_wg;
   const int64_t g1 = g0 + per_wg < total ? g0 + per_wg : total;
+  // the lane's (row, column) divided out once, then stepped
+  int64_t r = (g0 + threadIdx.x) / gpr, c = (g0 + threadIdx.x - r * gpr) * 8;
   for (int64_t g = g0 + threadIdx.x; g < g1; g += kThreads) {
-    const int64_t r = g / gpr, c = (g - r * gpr) * 8;
     const uint32_t sb = scales[r * ld_s + (c >> 5)];
+    const u32x2 w = __builtin_nontemporal_load((const u32x2*)(q + r * ldq + c));
     // 2^(sb-127): normal for sb >= 1, the subnormal 2^-127 for sb == 0
     const float X = sb == 0 ? __uint_as_float(0x00400000u) : __uint_as_float(sb << 23);
-    const u32x2 w = *(const u32x2*)(q + r * ldq + c);
     float o[8];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
@@ -916,13 +946,21 @@ __global__ __launch_bounds__(kThreads) void k_dequant_mx(const uint8_t* __restri
     }
     if constexpr (ODT == FP8Q_F32) {
       float* yp = (float*)y + r * ldy + c;
-      *(u32x4*)yp = u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
-      *((u32x4*)yp + 1) = u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])};
+      __builtin_nontemporal_store(
+          u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])}, (u32x4*)yp);
+      __builtin_nontemporal_store(
+          u32x4{__float_as_uint(o[4]), __float_as_uint(o[5]), __float_as_uint(o[6]), __float_as_uint(o[7])},
+          (u32x4*)yp + 1);
     } else {
       uint32_t b[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) b[k] = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o[2 * k], (__bf16)o[2 * k + 1]});
-      *(u32x4*)((uint16_t*)y + r * ldy + c) = u32x4{b[0], b[1], b[2], b[3]};
+      __builtin_nontemporal_store(u32x4{b[0], b[1], b[2], b[3]}, (u32x4*)((uint16_t*)y + r * ldy + c));
+    }
+    c += kThreads * 8;
+    while (c >= cols) {
+      c -= cols;
+      ++r;
     }
   }
 }
@@ -973,7 +1011,7 @@ int launch_quantize_tensor(const void* x, int dt, int64_t n, int fmt, const floa
   }
   const int64_t nvec = n / (dt == FP8Q_F32 ? 4 : 8);
   const int64_t ch = (int64_t)FP8Q_KU_T * FP8Q_TH_T;
-  const int grid = chunk_grid((nvec + ch - 1) / ch, FP8Q_G_T);
+  const int grid = chunk_grid((nvec + ch - 1) / ch, y ? FP8Q_G_TDQ : FP8Q_G_T);
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN)
     launch_qt<FP8Q_F32, FP8Q_E4M3FN>(grid, x, n, scale, q, amax, st, y, out_dt);
   else if (dt == FP8Q_F32)
@@ -1137,7 +1175,7 @@ int launch_dequantize_mx(const uint8_t* q, int fmt, int64_t rows, int64_t cols, 
                          int64_t ld_s, void* y, int out_dt, int64_t ldy, hipStream_t st) {
   const int64_t total = rows * (cols / 8);
   const int64_t steps = (total + kThreads - 1) / kThreads;
-  const int grid = chunk_grid(steps, FP8Q_G_D);
+  const int grid = chunk_grid(steps, FP8Q_G_DMX);
   const int64_t per_wg = ((steps + grid - 1) / grid) * kThreads;
   if (fmt == FP8Q_E4M3FN && out_dt == FP8Q_F32) launch_dqmx<FP8Q_E4M3FN, FP8Q_F32>(grid, q, rows, cols, ldq, scales, ld_s, y, ldy, per_wg, st);
   else if (fmt == FP8Q_E4M3FN) launch_dqmx<FP8Q_E4M3FN, FP8Q_BF16>(grid, q, rows, cols, ldq, scales, ld_s, y, ldy, per_wg, st);
