@@ -230,25 +230,32 @@ def run_gpu(steps: int, warmup: int):
     xhats = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(N_ROT)]
     for i in range(N_ROT):
         fq.fp8q_quantize_tensor(xs[i], n, fq.E4M3FN, sc_x, qxs[i])
+    # the quantizer rows write their codes (and round trips) to rotating
+    # outputs as well, so that no launch writes into lines a previous launch
+    # left in the last-level cache
+    qos = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(N_ROT)]
+    X_OUT = 3
+    qXos = [torch.empty(LM, LK, dtype=torch.uint8, device=dev) for _ in range(X_OUT)]
     per = {
         # the step's per-tensor quantizers: scale and amax accumulator in the scaler
         "quantize_tensor_x": per_launch(lambda r: fq.fp8q_quantize_tensor_delayed(xs[r % N_ROT], n, fq.E4M3FN, st_tmp,
-                                                                                  qx), 16),
+                                                                                  qos[r % N_ROT]), 16),
         "quantize_tensor_g": per_launch(lambda r: fq.fp8q_quantize_tensor_delayed(gs[r % N_ROT], n, fq.E5M2, st_tmp,
-                                                                                  qg), 16),
+                                                                                  qos[r % N_ROT]), 16),
         "quantize_tensor_dq_x": per_launch(lambda r: fq.fp8q_quantize_tensor_delayed(xs[r % N_ROT], n, fq.E4M3FN,
-                                                                                     st_tmp, qx, xhat), 16),
+                                                                                     st_tmp, qos[r % N_ROT],
+                                                                                     xhats[r % N_ROT]), 16),
         # the per-tensor quantizer with a caller's amax output, overwritten
         # (a one-thread reset launch, then the pass)
         "quantize_tensor_amax_out_x": per_launch(lambda r: fq.fp8q_quantize_tensor(xs[r % N_ROT], n, fq.E4M3FN, sc_x,
-                                                                                   qx, am_tmp), 16),
+                                                                                   qos[r % N_ROT], am_tmp), 16),
         "dequantize_x": per_launch(lambda r: fq.fp8q_dequantize(qxs[r % N_ROT], fq.E4M3FN, 1, n, n, sc_x, fq.GRAN_TENSOR,
                                                                 1, xhats[r % N_ROT], n), 16),
         "scaler_update": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_tmp, am_tmp), 16),
         "scaler_update_mean_1024": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_mean, am_tmp), 16),
         "scaler_update_ema_1024": per_launch(lambda r: fq.fp8q_delayed_scaler_update(st_ema, am_tmp), 16),
-        "quantize_1x128": per_launch(lambda r: fq.fp8q_quantize_1x128(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, 1e-12, qX, LK,
-                                                                       sX, LK // 128), 8),
+        "quantize_1x128": per_launch(lambda r: fq.fp8q_quantize_1x128(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, 1e-12,
+                                                                       qXos[r % X_OUT], LK, sX, LK // 128), 6),
         "gemm": per_launch(lambda r: fq.fp8q_gemm_blockscaled(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN, LK, sW,
                                                               fq.GRAN_128x128, LK // 128, 1, C, LN, LM, LN, LK), 4),
         "gemm_fast": per_launch(lambda r: fq.fp8q_gemm_blockscaled_fast(qX, fq.E4M3FN, LK, sX, LK // 128, 1, qW, fq.E4M3FN,
@@ -260,7 +267,7 @@ def run_gpu(steps: int, warmup: int):
     # reads and one write of the tensor)
     sX128 = torch.empty(LM // 128, LK // 128, dtype=torch.float32, device=dev)
     per["quantize_128x128"] = per_launch(lambda r: fq.fp8q_quantize_128x128(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, 1e-12,
-                                                                             qX, LK, sX128, LK // 128), 8)
+                                                                             qXos[r % X_OUT], LK, sX128, LK // 128), 6)
     per["amax_x"] = per_launch(lambda r: fq.fp8q_amax(xs[r % N_ROT], n, am_tmp), 16)
     st_w1 = torch.zeros(fq.SCALER_BYTES, dtype=torch.uint8, device=dev)
     fq.fp8q_delayed_scaler_init(st_w1, 1, 448.0, 1e-12, 1.0)
@@ -268,7 +275,7 @@ def run_gpu(steps: int, warmup: int):
     def current_scaling(r):
         fq.fp8q_amax(xs[r % N_ROT], n, am_tmp)
         fq.fp8q_delayed_scaler_update(st_w1, am_tmp)  # window 1: s = amax / 448
-        fq.fp8q_quantize_tensor_delayed(xs[r % N_ROT], n, fq.E4M3FN, st_w1, qx)
+        fq.fp8q_quantize_tensor_delayed(xs[r % N_ROT], n, fq.E4M3FN, st_w1, qos[r % N_ROT])
     per["current_scaling_x"] = per_launch(current_scaling, 8)
     # the same GEMM with its output quantized 1x128 (E4M3FN) in the epilogue
     qC = torch.empty(LM, LN, dtype=torch.uint8, device=dev)
@@ -285,7 +292,7 @@ def run_gpu(steps: int, warmup: int):
     # once, untimed.
     inputs = {"ds": (xs[0], gs[0]), "X": Xs[0], "qW": qW, "sW": sW}
     log("other GEMM shapes ...")
-    del xs, gs, qxs, xhats
+    del xs, gs, qxs, xhats, qos
     torch.cuda.empty_cache()
 
     def q1x128(x, fmt):
@@ -358,8 +365,8 @@ def run_gpu(steps: int, warmup: int):
     Xm = inputs["X"]
     qm = torch.empty(LM, LK, dtype=torch.uint8, device=dev)
     sm = torch.empty(LM, LK // 32, dtype=torch.uint8, device=dev)
-    per["quantize_mx"] = per_launch(lambda r: fq.fp8q_quantize_mx(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN, qm, LK, sm,
-                                                                  LK // 32), 16)
+    per["quantize_mx"] = per_launch(lambda r: fq.fp8q_quantize_mx(Xs[r % X_ROT], LM, LK, LK, fq.E4M3FN,
+                                                                  qXos[r % X_OUT], LK, sm, LK // 32), 12)
     # MX dequantize over four code / output sets (1.3 GB), past the last-level cache
     D_ROT = 4
     qms = [torch.empty(LM, LK, dtype=torch.uint8, device=dev) for _ in range(D_ROT)]
@@ -369,7 +376,7 @@ def run_gpu(steps: int, warmup: int):
         fq.fp8q_quantize_mx(Xs[i % X_ROT], LM, LK, LK, fq.E4M3FN, qms[i], LK, sms[i], LK // 32)
     per["dequantize_mx"] = per_launch(lambda r: fq.fp8q_dequantize_mx(qms[r % D_ROT], fq.E4M3FN, LM, LK, LK,
                                                                       sms[r % D_ROT], LK // 32, yms[r % D_ROT], LK), 16)
-    del qms, sms, yms
+    del qms, sms, yms, qXos
     wm = W.weight(LN, LK, seed=40, device=dev)
     qwm = torch.empty(LN, LK, dtype=torch.uint8, device=dev)
     swm = torch.empty(LN, LK // 32, dtype=torch.uint8, device=dev)
@@ -394,9 +401,12 @@ def run_gpu(steps: int, warmup: int):
 
 
 # Read / write bytes per item of the streaming reference (libfp8q_stream.so):
-# a copy, a bf16 quantizer's 2:1, an fp32 quantizer's 4:1 and a bf16
-# dequantizer's 1:2, each over about 1 GiB read.
-STREAM_KINDS = {"copy": (16, 16), "bf16_to_codes": (16, 8), "fp32_to_codes": (16, 4), "codes_to_bf16": (8, 16)}
+# a copy, a bf16 quantizer's 2:1, an fp32 quantizer's 4:1, a bf16
+# dequantizer's 1:2 (8-byte reads, or 16-byte reads and two 16-byte writes),
+# and a bf16 quantizer that also writes the bf16 round trip, 2:3 (codes and
+# values to two regions), each over about 1 GiB read.
+STREAM_KINDS = {"copy": (16, 16), "bf16_to_codes": (16, 8), "fp32_to_codes": (16, 4), "codes_to_bf16": (8, 16),
+                "codes_to_bf16_wide": (16, 32), "bf16_to_codes_and_bf16": (16, 24)}
 STREAM_READ_BYTES = 1 << 30
 
 
@@ -421,9 +431,10 @@ def stream_ceiling(dev, per_launch):
     for kind, (rd, wr) in STREAM_KINDS.items():
         items = STREAM_READ_BYTES // rd
         best = None
-        # 256-thread workgroups (the quantizers' size) and 1024-thread ones
-        sweep = [(256, u, g) for u in (2, 4, 8) for g in (4, 8, 16)] + \
-                [(1024, u, g) for u in (1, 2) for g in (1, 2, 4)]
+        # 256-thread workgroups (the quantizers' size) and 1024-thread ones,
+        # from a few long-lived workgroups per CU to many short ones
+        sweep = [(256, u, g) for u in (1, 2, 4, 8) for g in (4, 8, 16, 32, 64, 128)] + \
+                [(1024, u, g) for u in (1, 2) for g in (1, 2, 4, 8)]
         for th, u, g in sweep:
             def launch(r, u=u, g=g, th=th):
                 rc = L.fp8q_stream_ref(src.data_ptr(), dst.data_ptr(), items, rd, wr, u, g, cus, th,
@@ -559,9 +570,10 @@ def main():
     mx_tflops = alg["gemm_flop"] / (per["gemm_mx"] * 1e-3) / 1e12
     traffic = measured_traffic()
 
-    def fs(gbs, kind):
-        """Fraction of the measured stream ceiling of the same read:write proportion."""
-        return round(gbs / per["stream"][kind]["GB/s"], 4)
+    def fs(gbs, *kinds):
+        """Fraction of the measured stream ceiling of the same read:write
+        proportion (the fastest of the streams given)."""
+        return round(gbs / max(per["stream"][k]["GB/s"] for k in kinds), 4)
 
     out = {
         "metric": "quantize GB/s + block-scaled FP8 GEMM TFLOPS, % of HBM / FP8-MFMA peak",
@@ -622,7 +634,7 @@ def main():
                 "frac_hbm": round(gbps(alg["quantize_tensor_bytes"], per["quantize_tensor_amax_out_x"]) / HBM_PEAK_GBPS, 4),
                 "note": "fp8q_quantize_tensor with its amax output overwritten: a one-thread reset launch, then the pass"},
             "quantize_tensor_dq_bf16_e4m3": {"ms": round(per["quantize_tensor_dq_x"], 4), "GB/s": round(q_dq, 1),
-                                             "frac_hbm": round(q_dq / HBM_PEAK_GBPS, 4), "frac_stream": fs(q_dq, "copy"),
+                                             "frac_hbm": round(q_dq / HBM_PEAK_GBPS, 4), "frac_stream": fs(q_dq, "bf16_to_codes_and_bf16"),
                                              "note": "codes and their bf16 round trip in one pass (the step's x)"},
             "quantize_128x128_bf16": {
                 "ms": round(per["quantize_128x128"], 4),
@@ -639,7 +651,7 @@ def main():
                 "note": "current scaling: amax, the scale from it, then the quantize (two reads + one write)"},
             "dequantize_bf16": {"ms": round(per["dequantize_x"], 4), "GB/s": round(dq, 1),
                                 "frac_hbm": round(dq / HBM_PEAK_GBPS, 4),
-                                "frac_stream": fs(dq, "codes_to_bf16")},
+                                "frac_stream": fs(dq, "codes_to_bf16", "codes_to_bf16_wide")},
             "scaler_update": {"ms": round(per["scaler_update"], 4)},
             "scaler_update_mean_1024": {"ms": round(per["scaler_update_mean_1024"], 4),
                                         "note": "window mean over 1024 slots (fp64 pairwise)"},
@@ -667,7 +679,7 @@ def main():
                                  "note": "MX E4M3FN, 32-element blocks, E8M0 scales; the layer's activation"},
             "dequantize_mx_bf16": {"ms": round(per["dequantize_mx"], 4), "GB/s": round(dq_mx, 1),
                                    "frac_hbm": round(dq_mx / HBM_PEAK_GBPS, 4),
-                                   "frac_stream": fs(dq_mx, "codes_to_bf16")},
+                                   "frac_stream": fs(dq_mx, "codes_to_bf16", "codes_to_bf16_wide")},
             "gemm_mx": {"ms": round(per["gemm_mx"], 4), "TFLOP/s": round(mx_tflops, 2),
                         "frac_fp8_peak": round(mx_tflops / FP8_PEAK_TFLOPS, 4),
                         "operands": "MX E4M3FN x MX E4M3FN, scaled FP8 MFMA, bf16 out, the layer's shape"},

@@ -93,19 +93,19 @@ __global__ void k_set_u32(uint32_t* p, uint32_t v) { *p = v; }
 #define FP8Q_TH_T 256  // threads per workgroup of the per-tensor quantizer
 #endif
 #ifndef FP8Q_G_MX
-#define FP8Q_G_MX 32
+#define FP8Q_G_MX 128
 #endif
 #ifndef FP8Q_KU_MX
-#define FP8Q_KU_MX 4
+#define FP8Q_KU_MX 1
 #endif
 #ifndef FP8Q_G_1
-#define FP8Q_G_1 32
+#define FP8Q_G_1 64
 #endif
 #ifndef FP8Q_KU_D
-#define FP8Q_KU_D 4
+#define FP8Q_KU_D 2
 #endif
 #ifndef FP8Q_G_D
-#define FP8Q_G_D 32
+#define FP8Q_G_D 64
 #endif
 #ifndef FP8Q_G_DMX
 #define FP8Q_G_DMX 128
@@ -192,19 +192,17 @@ __device__ __forceinline__ float canon_nan(float f) {
 // NaN made 0x7FC00000, written as fp32 or RNE bf16 at element i4 of y --
 // the arithmetic of fp8q_dequantize, so the fused output matches it bit
 // for bit.
-// The round-trip values are stored with plain (cached) stores: beside the
-// codes' nontemporal stores they measured 10% faster than nontemporal ones
-// (8192x8192 bf16, codes + bf16 round trip).
 template <int FMT, int ODT>
 __device__ __forceinline__ void store_dq4(uint32_t w, float s, void* __restrict__ y, int64_t i4) {
   const float2 lo = dec2<FMT>(w, false), hi = dec2<FMT>(w, true);
   const float o0 = canon_nan(lo.x * s), o1 = canon_nan(lo.y * s), o2 = canon_nan(hi.x * s), o3 = canon_nan(hi.y * s);
   if constexpr (ODT == FP8Q_F32) {
-    *(u32x4*)((float*)y + i4) = u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)};
+    __builtin_nontemporal_store(u32x4{__float_as_uint(o0), __float_as_uint(o1), __float_as_uint(o2), __float_as_uint(o3)},
+                                (u32x4*)((float*)y + i4));
   } else {
     const uint32_t a = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o0, (__bf16)o1});
     const uint32_t b = __builtin_bit_cast(uint32_t, v2bf16{(__bf16)o2, (__bf16)o3});
-    *(u32x2*)((uint16_t*)y + i4) = u32x2{a, b};
+    __builtin_nontemporal_store(u32x2{a, b}, (u32x2*)((uint16_t*)y + i4));
   }
 }
 
@@ -473,9 +471,6 @@ __global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict_
   // 16-byte writes whole and the column-wise reads free of bank conflicts.
   auto swz = [](int t) { return DT == FP8Q_F32 ? 16 * ((t >> 4) & 3) : 16 * ((t >> 4) & (W / 16 - 1)); };
   // One row block: stage the tile, reduce each column's amax, encode, store.
-  // The codes leave through plain stores: their 128-byte runs per column
-  // (columns ldq bytes apart) measured 4-5% faster than with nontemporal
-  // stores.
   auto block = [&](int64_t rb, const u32x4* v) {
 #pragma unroll
     for (int i = 0; i < NVT; ++i) {
@@ -516,8 +511,8 @@ __global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict_
         for (int i = 0; i < 8; ++i) w[i] = quant4_exact<FMT>(a[4 * i], a[4 * i + 1], a[4 * i + 2], a[4 * i + 3], s);
       }
       uint8_t* qrow = q + col * ldq + rb * 128 + 16 * k;
-      *(u32x4*)qrow = u32x4{w[0], w[1], w[2], w[3]};
-      *(u32x4*)(qrow + 64) = u32x4{w[4], w[5], w[6], w[7]};
+      __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)qrow);
+      __builtin_nontemporal_store(u32x4{w[4], w[5], w[6], w[7]}, (u32x4*)(qrow + 64));
     } else {
       const int p = tid >> 3, k = tid & 7;
       const int pc = p ^ (8 * (k & (W / 16 - 1)));  // the pair's slot in rows 16k .. 16k+16
@@ -555,7 +550,7 @@ __global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict_
 #pragma unroll
           for (int i = 0; i < 4; ++i) w[i] = quant4_exact<FMT>(val(4 * i), val(4 * i + 1), val(4 * i + 2), val(4 * i + 3), s);
         }
-        *(u32x4*)(q + col * ldq + rb * 128 + 16 * k) = u32x4{w[0], w[1], w[2], w[3]};
+        __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)(q + col * ldq + rb * 128 + 16 * k));
       }
     }
   };
@@ -579,10 +574,7 @@ __global__ __launch_bounds__(4 * W) void k_quant_1x128_t(const void* __restrict_
 // ---------------------------------------------------------------- 128x128
 // One workgroup per 128x128 tile: the tile is read into registers once
 // (bf16: 8 rows x 16 B per thread; fp32: 16 rows x 16 B), its amax found
-// by a workgroup reduction, then quantized from the registers.  The codes
-// leave through plain stores: 5% faster than nontemporal ones on a
-// 16384x7168 bf16 input (the other quantizers measured faster with
-// nontemporal stores and keep them).
+// by a workgroup reduction, then quantized from the registers.
 template <int DT, int FMT>
 __global__ __launch_bounds__(kThreads) void k_quant_128x128(const void* __restrict__ x, int64_t nkb,
                                                             int64_t ldx, float eps,
@@ -627,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_128x128(const void* __restri
       uint32_t w = fast ? pack4<FMT>(sat<FMT>(div_rn(a, s, r)), sat<FMT>(div_rn(b, s, r)),
                                      sat<FMT>(div_rn(cc, s, r)), sat<FMT>(div_rn(d, s, r)))
                         : quant4_exact<FMT>(a, b, cc, d, s);
-      *(uint32_t*)(qr + 4 * c) = w;
+      __builtin_nontemporal_store(w, (uint32_t*)(qr + 4 * c));
     } else {
       float e[8] = {bf_lo(v[i].x), bf_hi(v[i].x), bf_lo(v[i].y), bf_hi(v[i].y),
                     bf_lo(v[i].z), bf_hi(v[i].z), bf_lo(v[i].w), bf_hi(v[i].w)};
@@ -641,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_128x128(const void* __restri
         w.x = quant4_exact<FMT>(e[0], e[1], e[2], e[3], s);
         w.y = quant4_exact<FMT>(e[4], e[5], e[6], e[7], s);
       }
-      *(u32x2*)(qr + 8 * c) = w;
+      __builtin_nontemporal_store(w, (u32x2*)(qr + 8 * c));
     }
   }
 }

@@ -8,7 +8,11 @@
 //   (16, 16)  a copy,
 //   (16, 8)   bf16 in, one byte per element out (a bf16 quantizer),
 //   (16, 4)   fp32 in, one byte per element out (an fp32 quantizer),
-//   (8, 16)   one byte per element in, bf16 out (a dequantizer).
+//   (8, 16)   one byte per element in, bf16 out (a dequantizer),
+//   (16, 32)  the same proportion with 16-byte reads and two 16-byte writes,
+//   (16, 24)  bf16 in, a byte and a bf16 out per element (a quantizer that
+//             also writes the round trip; the 8-byte and 16-byte parts go
+//             to two regions of the output, as codes and values would).
 // The written words are xor folds (or copies) of the read ones, so nothing
 // can be dropped, and no arithmetic competes with the memory traffic.  Work
 // is cut into contiguous chunks of U items per lane, walked by a persistent
@@ -43,6 +47,12 @@ __global__ __launch_bounds__(TH) void k_stream(const uint8_t* __restrict__ in, u
       if (i >= nitems) break;
       if constexpr (RB == 8) {
         __builtin_nontemporal_store(u32x4{v[u].x, v[u].y, v[u].x ^ v[u].y, v[u].y}, (u32x4*)out + i);
+      } else if constexpr (WB == 32) {
+        __builtin_nontemporal_store(v[u], (u32x4*)out + 2 * i);
+        __builtin_nontemporal_store(u32x4{v[u].y, v[u].x, v[u].w, v[u].z}, (u32x4*)out + 2 * i + 1);
+      } else if constexpr (WB == 24) {
+        __builtin_nontemporal_store(u32x2{v[u].x ^ v[u].y, v[u].z ^ v[u].w}, (u32x2*)out + i);
+        __builtin_nontemporal_store(v[u], (u32x4*)(out + 8 * nitems) + i);
       } else if constexpr (WB == 16) {
         __builtin_nontemporal_store(v[u], (u32x4*)out + i);
       } else if constexpr (WB == 8) {
@@ -76,7 +86,9 @@ hipError_t launch_k(int u, int threads, int grid, const uint8_t* in, uint8_t* ou
 extern "C" {
 
 // in: items * rd bytes, out: items * wr bytes, both 16-B aligned, with
-// (rd, wr) one of (16, 16), (16, 8), (16, 4), (8, 16); vectors_per_lane in
+// (rd, wr) one of (16, 16), (16, 8), (16, 4), (8, 16), (16, 32), (16, 24)
+// (for (16, 24) items must be even, so the 16-byte part stays aligned);
+// vectors_per_lane in
 // {1, 2, 4, 8}; threads (per workgroup) 256 or 1024; the grid is
 // wg_per_cu * cu_count workgroups (the caller passes the device's
 // compute-unit count, so nothing is queried while a graph is being
@@ -87,7 +99,8 @@ int fp8q_stream_ref(const void* in, void* out, int64_t items, int rd, int wr, in
   if (!in || !out || items <= 0 || ((uintptr_t)in | (uintptr_t)out) % 16 != 0 || wg_per_cu < 1 || cu_count < 1 ||
       (threads != 256 && threads != 1024))
     return -1;
-  const bool ok = (rd == 16 && (wr == 16 || wr == 8 || wr == 4)) || (rd == 8 && wr == 16);
+  const bool ok = (rd == 16 && (wr == 32 || wr == 24 || wr == 16 || wr == 8 || wr == 4)) || (rd == 8 && wr == 16);
+  if (wr == 24 && (items & 1)) return -1;
   const int u = vectors_per_lane;
   if (!ok || (u != 1 && u != 2 && u != 4 && u != 8)) return -1;
   const int cus = cu_count;
@@ -100,6 +113,10 @@ int fp8q_stream_ref(const void* in, void* out, int64_t items, int rd, int wr, in
   hipError_t e;
   if (rd == 8)
     e = launch_k<8, 16>(u, threads, grid, src, dst, items, st);
+  else if (wr == 32)
+    e = launch_k<16, 32>(u, threads, grid, src, dst, items, st);
+  else if (wr == 24)
+    e = launch_k<16, 24>(u, threads, grid, src, dst, items, st);
   else if (wr == 16)
     e = launch_k<16, 16>(u, threads, grid, src, dst, items, st);
   else if (wr == 8)
