@@ -119,6 +119,29 @@ def test_quantize_mx_full_activation(fq, orc, gpu):
     assert_equal_bytes(q[rows], wq, "codes")
 
 
+@pytest.mark.parametrize("rows,cols", [(2_200_000, 32), (740_000, 96)])
+def test_mx_narrow_rows_many_passes(fq, orc, gpu, rows, cols):
+    """Tensors large enough that every workgroup of the MX quantizer and
+    dequantizer makes several passes, with rows narrower than one pass (a
+    lane's row and column are stepped across many rows per pass): codes and
+    scale bytes, then the bf16 dequantization, bit-exact on sampled rows
+    (the first, the last, and rows spread over the whole tensor)."""
+    x = W.activation(rows, cols, seed=rows + cols, factor=1e3, dtype=torch.bfloat16, device=gpu)
+    q = torch.empty(rows, cols, dtype=torch.uint8, device=gpu)
+    s = torch.empty(rows, cols // 32, dtype=torch.uint8, device=gpu)
+    fq.fp8q_quantize_mx(x, rows, cols, cols, E4, q, cols, s, cols // 32)
+    y = torch.empty(rows, cols, dtype=torch.bfloat16, device=gpu)
+    fq.fp8q_dequantize_mx(q, E4, rows, cols, cols, s, cols // 32, y, cols)
+    torch.cuda.synchronize()
+    idx = np.unique(np.concatenate([np.linspace(0, rows - 1, 997).astype(np.int64), [1, 2, rows - 2, rows - 1]]))
+    ti = torch.from_numpy(idx).to(gpu)
+    wq, ws = orc.quantize_mx(W.to_numpy_input(x[ti].cpu()), E4)
+    assert_equal_bytes(s[ti].cpu().numpy(), ws, "scale bytes")
+    assert_equal_bytes(q[ti].cpu().numpy(), wq, "codes")
+    want = torch.from_numpy(orc.dequantize_mx(wq, E4, ws)).to(torch.bfloat16)
+    assert_equal_bytes(y[ti].cpu().view(torch.int16).numpy(), want.view(torch.int16).numpy(), "bf16")
+
+
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("fmt", [E4, E5])
 @pytest.mark.parametrize("rows,cols,padq,pads,pady", [(5, 64, 0, 0, 0), (257, 1024, 16, 2, 8), (64, 4096, 0, 0, 0)])

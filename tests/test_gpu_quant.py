@@ -502,6 +502,22 @@ def test_dequantize_strided(fq, orc, gpu, gran, rows, cols, ld, out):
     assert np.all(got[:, cols:] == pad), "dequantize wrote past the row"
 
 
+@pytest.mark.parametrize("gran,rows,cols", [(0, 1, 70_000_000), (1, 40_000, 128), (2, 40_100, 256)])
+def test_dequantize_many_passes(fq, orc, gpu, gran, rows, cols):
+    """More work units (a row's chunk of 4096 codes) than the grid has
+    workgroups, so every workgroup walks several units: bf16 bit-exact
+    against the oracle over the whole tensor."""
+    q = W.fp8_codes((rows, cols), E4, seed=rows + cols)
+    rng = np.random.default_rng(rows)
+    shape = {0: (1, 1), 1: (rows, cols // 128), 2: ((rows + 127) // 128, cols // 128)}[gran]
+    s = np.exp(rng.standard_normal(shape) * 3).astype(np.float32)
+    y = torch.empty(rows, cols, dtype=torch.bfloat16, device=gpu)
+    fq.fp8q_dequantize(q.to(gpu), E4, rows, cols, cols, torch.from_numpy(s).to(gpu), gran, shape[1], y, cols)
+    torch.cuda.synchronize()
+    want = orc.dequantize(q.numpy(), E4, s, gran, out_bf16=True)
+    assert np.array_equal(y.cpu().view(torch.int16).numpy().view(np.uint16), want.view(np.uint16))
+
+
 def test_dequantize_flat_ragged(fq, orc, gpu):
     n = 10_007
     q = W.fp8_codes((n,), E4, seed=8)
