@@ -93,16 +93,6 @@ __device__ __forceinline__ v2bf dec2_bf16(uint32_t w) {
     return __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8((int)w, 1.0f, HI);
 }
 
-template <int FMT>
-__device__ __forceinline__ v8bf dec8_bf16(u32x2 w) {
-  const v2bf a = dec2_bf16<FMT, false>(w.x), b = dec2_bf16<FMT, true>(w.x);
-  const v2bf c = dec2_bf16<FMT, false>(w.y), d = dec2_bf16<FMT, true>(w.y);
-  v8bf r;
-  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-  return r;
-}
-
 // With an E5M2 operand the exact path multiplies in f16 instead: an E5M2
 // code is the upper byte of the f16 of the same value, so its conversion
 // is one byte permute per two codes (against one 8-cycle conversion on
