@@ -295,8 +295,8 @@ __global__ __launch_bounds__(FP8Q_TH_T) void k_quant_tensor(const void* __restri
 }
 
 // ---------------------------------------------------------------- 1x128
-// Each 16-lane DPP row of a wavefront owns one 128-element block: 16 lanes
-// x 16 bytes is the whole block for bf16, and two such loads for fp32
+// fp32 inputs (bf16 ones take k_quant_1x128_b8 below): each 16-lane DPP row
+// of a wavefront owns one 128-element block, two 16-byte loads per lane
 // (element offsets 4l and 64+4l).  A wavefront takes kGroups groups of four
 // consecutive blocks, all loads in flight at once; a workgroup's four
 // wavefronts cover consecutive stretches, so each workgroup streams one
@@ -410,6 +410,95 @@ __global__ __launch_bounds__(kThreads) void k_quant_1x128(const void* __restrict
       if (ok[g])
         quant_block_regs<DT, FMT>(v[g], am, eps, q + row[g] * ldq + 128 * kb[g],
                                   scales + row[g] * ld_s + kb[g], l);
+    }
+  }
+}
+
+// bf16 inputs: eight lanes per block.  Lane l of a block holds its elements
+// 16l .. 16l+16 (two 16-byte loads), the block maximum is reduced over the
+// eight lanes, and the lane's 16 codes leave in one 16-byte store; the
+// per-block scale arithmetic is then shared by 16 elements per lane instead
+// of 8 (64.7 -> 60.4-60.9 us on the 16384x7168 activation against the
+// sixteen-lane form, bit-identical).  A wavefront takes FP8Q_KG8 groups of
+// eight consecutive blocks per chunk; FP8Q_G_B8 workgroups per CU.
+#ifndef FP8Q_G_B8
+#define FP8Q_G_B8 128
+#endif
+#ifndef FP8Q_KG8
+#define FP8Q_KG8 1
+#endif
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void k_quant_1x128_b8(const void* __restrict__ x, int64_t nkb,
+                                                             int64_t nblocks, int64_t ldx, float eps,
+                                                             uint8_t* __restrict__ q, int64_t ldq,
+                                                             float* __restrict__ scales, int64_t ld_s) {
+  constexpr int G = FP8Q_KG8;
+  constexpr int64_t kWaveBlocks = 8 * G;
+  constexpr int64_t kBlocks = kWaveBlocks * (kThreads / 64);
+  const int lane = threadIdx.x & 63;
+  const int rr = lane >> 3, l = lane & 7;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* xb = (const char*)x;
+  for (int64_t c = blockIdx.x; c * kBlocks < nblocks; c += gridDim.x) {
+    const int64_t b0 = c * kBlocks + wave * kWaveBlocks;
+    int64_t rg = b0 / nkb, kg = b0 - rg * nkb;
+    u32x4 v[G][2];
+    int64_t row[G], kb[G];
+    bool ok[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (g > 0) {
+        kg += 8;
+        while (kg >= nkb) { kg -= nkb; ++rg; }
+      }
+      int64_t r0 = rg, k0 = kg + rr;
+      while (k0 >= nkb) { k0 -= nkb; ++r0; }
+      row[g] = r0;
+      kb[g] = k0;
+      ok[g] = b0 + 8 * g + rr < nblocks;
+      if (ok[g]) {
+        const u32x4* p = (const u32x4*)(xb + (r0 * ldx + 128 * k0) * 2);
+        v[g][0] = __builtin_nontemporal_load(p + 2 * l);
+        v[g][1] = __builtin_nontemporal_load(p + 2 * l + 1);
+      } else {
+        v[g][0] = v[g][1] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      uint32_t pm = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        pm = pk_absmax(pk_absmax(pm, v[g][h].x), v[g][h].y);
+        pm = pk_absmax(pk_absmax(pm, v[g][h].z), v[g][h].w);
+      }
+      uint32_t m = pk_fold(pm);
+      m = max(m, (uint32_t)__shfl_xor((int)m, 1));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+      m = max(m, (uint32_t)__shfl_xor((int)m, 4));
+      if (!ok[g]) continue;
+      const float s = block_scale<FMT>(__uint_as_float(canon_abs_bits(m)), eps);
+      if (l == 0) scales[row[g] * ld_s + kb[g]] = s;
+      uint32_t w[4];
+      if (scale_ok(s)) {
+        const float r = 1.0f / s;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 t = v[g][h];
+          w[2 * h] = pack4<FMT>(sat<FMT>(div_rn(bf_lo(t.x), s, r)), sat<FMT>(div_rn(bf_hi(t.x), s, r)),
+                                sat<FMT>(div_rn(bf_lo(t.y), s, r)), sat<FMT>(div_rn(bf_hi(t.y), s, r)));
+          w[2 * h + 1] = pack4<FMT>(sat<FMT>(div_rn(bf_lo(t.z), s, r)), sat<FMT>(div_rn(bf_hi(t.z), s, r)),
+                                    sat<FMT>(div_rn(bf_lo(t.w), s, r)), sat<FMT>(div_rn(bf_hi(t.w), s, r)));
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 t = v[g][h];
+          w[2 * h] = quant4_exact<FMT>(bf_lo(t.x), bf_hi(t.x), bf_lo(t.y), bf_hi(t.y), s);
+          w[2 * h + 1] = quant4_exact<FMT>(bf_lo(t.z), bf_hi(t.z), bf_lo(t.w), bf_hi(t.w), s);
+        }
+      }
+      __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (u32x4*)(q + row[g] * ldq + 128 * kb[g] + 16 * l));
     }
   }
 }
@@ -1031,8 +1120,16 @@ int launch_quantize_1x128(const void* x, int dt, int64_t rows, int64_t cols, int
   const int grid = chunk_grid((nblocks + per_chunk - 1) / per_chunk, FP8Q_G_1);
   if (dt == FP8Q_F32 && fmt == FP8Q_E4M3FN) launch_q1<FP8Q_F32, FP8Q_E4M3FN>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
   else if (dt == FP8Q_F32) launch_q1<FP8Q_F32, FP8Q_E5M2>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
-  else if (fmt == FP8Q_E4M3FN) launch_q1<FP8Q_BF16, FP8Q_E4M3FN>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
-  else launch_q1<FP8Q_BF16, FP8Q_E5M2>(grid, x, nkb, nblocks, ldx, eps, q, ldq, scales, ld_s, st);
+  else {
+    const int64_t pc8 = 8 * FP8Q_KG8 * (kThreads / 64);
+    const int g8 = chunk_grid((nblocks + pc8 - 1) / pc8, FP8Q_G_B8);
+    if (fmt == FP8Q_E4M3FN)
+      hipLaunchKernelGGL((k_quant_1x128_b8<FP8Q_E4M3FN>), dim3(g8), dim3(kThreads), 0, st, x, nkb, nblocks, ldx, eps,
+                         q, ldq, scales, ld_s);
+    else
+      hipLaunchKernelGGL((k_quant_1x128_b8<FP8Q_E5M2>), dim3(g8), dim3(kThreads), 0, st, x, nkb, nblocks, ldx, eps,
+                         q, ldq, scales, ld_s);
+  }
   return check_launch("quantize_1x128");
 }
 
